@@ -1,0 +1,8 @@
+"""CPU oracle for the StagQ batch-one GEMV (test infrastructure only).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg import this
+package.  It shares no code with the HIP library.
+"""
+from .stagq_oracle import (  # noqa: F401
+    Fields, encode, quantize_value, codes, w_main, w_hat, gemv, half_step, affine_pair, budget,
+)

@@ -1,0 +1,282 @@
+"""Plain CPU oracle for the StagQ batch-one GEMV.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module; the product path (the HIP library
+and its Python binding) never does.  It shares no code with the product: every
+step below is written from the StagQ paper ("StagQ: Constraint-Driven
+Multi-Precision Weight Quantization for LLMs"), in float64 NumPy, slowly and
+in the paper's order, so that a reader can check it against the text by eye.
+
+What is computed
+----------------
+encode()      the reference encoder.  The paper's encoder (section 3.6,
+              Figure 3, Appendix E) runs pre-grid guard -> pair fit -> base
+              code -> post-grid guard -> planes.  Calibration data are not
+              available, so the activation scale is omitted and every weight
+              counts equally (E_c = 1); the pair is the conventional min-max
+              lattice of section 3.1 / Appendix D; the pre-grid guard is the
+              ratio criterion of section 3.5.
+codes()       the composite integer u_M of Eq. (8).
+w_main()      the additive reconstruction of Eq. (9) (the direct form; the GPU
+              path uses the affine collapse of Eq. (10) instead).
+w_hat()       the complete reconstruction of Eq. (4): main stream outside the
+              side record, the recorded value inside it.
+gemv()        y = W_hat^(M) x in float64.
+
+Readings of the paper (where it is silent or leaves a choice open)
+------------------------------------------------------------------
+R1  "Nearest rounding" of the base code breaks ties upward, the same way the
+    planes treat a zero residual (sign(0) := +1, section 3.3).
+R2  The pair is fitted to the non-held-out entries of the group: lo = min,
+    s = (max - min)/3, so the outer two base levels sit on the group extremes
+    (the conventional four-level lattice of section 3.1).  This equals the
+    paper's "held-out entry clipped to the next value inward".  The pair is
+    stored as two fp16 numbers; every later step uses the stored values.
+R3  Pre-grid guard = ratio criterion with T = 4 (section 3.5, Table 6): in
+    each group, the largest |w| (lowest column on ties) is a candidate when it
+    exceeds T times the second largest.  Candidates are ranked by that ratio
+    (infinite when the second largest is 0; ties by flat index) and the first
+    min(K, #candidates) are held out, K = round(frac * R * C).
+R4  Post-grid guard: the remaining budget K - K_pre goes to the entries with
+    the largest two-bit residual |w - (lo + s q)| over the whole matrix (ties
+    by flat index).  The paper picks per output row with activation weights
+    (Appendix E); without calibration data a global unweighted pick is used.
+R5  Held-out entries keep the base code of their original value and all-zero
+    planes: the planes "skip every position the side record already carries"
+    (section 3.6), and Eq. (4)'s (1 - m) removes whatever the main stream
+    decodes there.
+R6  The side record stores the held-out weight itself as fp16.  For fp16
+    weights this equals both of the paper's definitions of P (section 3).
+R7  A group whose stored step is 0 gets q = 0 and all-zero planes.
+
+Parity status of every function is recorded next to it ("pinned by ...").
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "Fields", "encode", "quantize_value", "codes", "w_main", "w_hat", "gemv",
+    "half_step", "affine_pair", "budget",
+]
+
+
+@dataclass
+class Fields:
+    """Unpacked encoder output (the fields the main stream and side record hold)."""
+    rows: int
+    cols: int
+    group: int
+    nbits: int                 # N: q plus planes k = 3..N
+    q: np.ndarray              # uint8 [R, C], 0..3
+    planes: np.ndarray         # uint8 [N-2, R, C], 0/1, plane k = 3 first
+    lo: np.ndarray             # float16 [R, G]
+    s: np.ndarray              # float16 [R, G]
+    mask: np.ndarray           # bool [R, C], held-out entries (m of Eq. 4)
+    row_ptr: np.ndarray        # int32 [R + 1]
+    col: np.ndarray            # int32 [nnz]
+    val: np.ndarray            # float16 [nnz], the recorded value P
+    n_pre: int = 0             # entries held out by the pre-grid guard
+    n_post: int = 0            # entries held out by the post-grid guard
+
+    @property
+    def nnz(self) -> int:
+        return int(self.col.shape[0])
+
+    def as_dict(self) -> Dict[str, np.ndarray]:
+        return dict(q=self.q, planes=self.planes, lo=self.lo, s=self.s, mask=self.mask,
+                    row_ptr=self.row_ptr, col=self.col, val=self.val)
+
+
+def budget(frac: float, rows: int, cols: int) -> int:
+    """Side-record size K = round(frac * R * C), halves rounded up."""
+    return int(np.floor(frac * rows * cols + 0.5))
+
+
+# ---------------------------------------------------------------------------
+# Single-value quantizer (section 3.3 digit maps, section 3.6 plane rule).
+# Pinned by the Figure 1 worked example and the closed-form code test.
+# ---------------------------------------------------------------------------
+def quantize_value(w: float, lo: float, s: float, nbits: int):
+    """Quantize one value against a pair (lo, s): returns (q, [b_3..b_N]).
+
+    q is the nearest of the four base levels lo + j*s (ties upward, R1); each
+    plane bit is the sign of the residual left by the prefix before it, with
+    sign(0) := +1, and moves the reconstruction by +-s/2^(k-1) (Eq. 7).
+    """
+    w = float(w); lo = float(lo); s = float(s)
+    if s == 0.0:
+        return 0, [0] * (nbits - 2)
+    q = sum(1 for j in range(3) if w - lo >= (j + 0.5) * s)
+    rec = lo + s * q
+    bits = []
+    for k in range(3, nbits + 1):
+        b = 1 if w - rec >= 0.0 else 0
+        rec += (2 * b - 1) * s / 2.0 ** (k - 1)
+        bits.append(b)
+    return q, bits
+
+
+def half_step(s, M: int):
+    """t_M = s / 2^(M-1), the half-step of the deepest plane read (Eq. 7)."""
+    return s / 2.0 ** (M - 1)
+
+
+def affine_pair(lo, s, M: int):
+    """(lo_M, s_M) of Eq. (10): s_M = s/2^(M-2), lo_M = lo - s(2^(M-2)-1)/2^(M-1)."""
+    return lo - s * (2.0 ** (M - 2) - 1.0) / 2.0 ** (M - 1), s / 2.0 ** (M - 2)
+
+
+# ---------------------------------------------------------------------------
+# Encoder (section 3.6 order).  Pinned by hand-worked small matrices in
+# tests/golden/encoder_small.json, the Figure 1 example and the invariants.
+# ---------------------------------------------------------------------------
+def encode(w16: np.ndarray, group: int, nbits: int, frac: float, T: float = 4.0) -> Fields:
+    w16 = np.asarray(w16)
+    if w16.ndim != 2 or w16.dtype not in (np.float16, np.float64):
+        raise ValueError("encode expects a 2-D float16 (or float64, statistics only) matrix")
+    R, C = w16.shape
+    if C % group != 0:
+        raise ValueError("cols must be a multiple of the group size")
+    if nbits < 2:
+        raise ValueError("nbits must be >= 2")
+    G = C // group
+    w = w16.astype(np.float64)                      # exact
+    wg = w.reshape(R, G, group)
+    flat = np.arange(R * C, dtype=np.int64).reshape(R, G, group)
+    K = budget(frac, R, C)
+    mask = np.zeros((R, G, group), dtype=bool)
+
+    # 1. Pre-grid guard, ratio criterion (section 3.5, R3).
+    mag = np.abs(wg)
+    i_max = np.argmax(mag, axis=2)                  # first maximum = lowest column
+    a = np.take_along_axis(mag, i_max[..., None], axis=2)[..., 0]
+    others = mag.copy()
+    np.put_along_axis(others, i_max[..., None], -1.0, axis=2)
+    b = others.max(axis=2)
+    is_cand = a > T * b
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(b > 0.0, a / np.where(b > 0.0, b, 1.0), np.inf)
+    cand_r, cand_g = np.nonzero(is_cand)
+    cand_flat = flat[cand_r, cand_g, i_max[cand_r, cand_g]]
+    cand_ratio = ratio[cand_r, cand_g]
+    order = np.lexsort((cand_flat, -cand_ratio))     # ratio descending, then flat index
+    n_pre = min(K, order.shape[0])
+    keep = order[:n_pre]
+    mask[cand_r[keep], cand_g[keep], i_max[cand_r[keep], cand_g[keep]]] = True
+
+    # 2. Pair fit over the entries that stay in the main stream (R2).
+    lo64 = np.where(mask, np.inf, wg).min(axis=2)
+    hi64 = np.where(mask, -np.inf, wg).max(axis=2)
+    lo16 = lo64.astype(np.float16)                  # exact for fp16 weights
+    s16 = ((hi64 - lo64) / 3.0).astype(np.float16)  # round to nearest even
+    lo_f = lo16.astype(np.float64)[..., None]
+    s_f = s16.astype(np.float64)[..., None]
+
+    # 3. Base code: nearest of lo + j s, ties upward (R1); all entries, including
+    #    the pre-grid ones, from their original values (R5); s = 0 -> q = 0 (R7).
+    d = wg - lo_f
+    q = np.zeros((R, G, group), dtype=np.int64)
+    for j in range(3):
+        q += (d >= (j + 0.5) * s_f)
+    q = np.where(s_f > 0.0, q, 0)
+
+    # 4. Post-grid guard: largest two-bit residuals over the matrix (R4).
+    r2 = np.abs(wg - (lo_f + s_f * q))
+    n_post = K - n_pre
+    if n_post > 0:
+        free_flat = flat[~mask]
+        free_r2 = r2[~mask]
+        order = np.lexsort((free_flat, -free_r2))
+        pick = free_flat[order[:n_post]]
+        mask.reshape(-1)[pick] = True
+
+    # 5. Planes: sign of the residual of the preceding prefix (sections 3.3, 3.6);
+    #    skipped (0) at held-out positions and in zero-step groups (R5, R7).
+    planes = np.zeros((nbits - 2, R, G, group), dtype=np.uint8)
+    rec = lo_f + s_f * q
+    active = (~mask) & (s_f > 0.0)
+    for k in range(3, nbits + 1):
+        bk = ((wg - rec) >= 0.0) & active
+        planes[k - 3] = bk
+        rec = rec + np.where(active, (2.0 * bk - 1.0) * s_f / 2.0 ** (k - 1), 0.0)
+
+    # 6. Side record as CSR sorted by (row, col), the recorded value = w (R6).
+    mask2 = mask.reshape(R, C)
+    rr, cc = np.nonzero(mask2)                      # row-major order = (row, col) sorted
+    row_ptr = np.zeros(R + 1, dtype=np.int64)
+    np.add.at(row_ptr, rr + 1, 1)
+    row_ptr = np.cumsum(row_ptr).astype(np.int32)
+    return Fields(
+        rows=R, cols=C, group=group, nbits=nbits,
+        q=q.reshape(R, C).astype(np.uint8),
+        planes=planes.reshape(nbits - 2, R, C),
+        lo=lo16, s=s16, mask=mask2,
+        row_ptr=row_ptr, col=cc.astype(np.int32), val=w16[rr, cc].astype(np.float16),
+        n_pre=int(n_pre), n_post=int(max(n_post, 0)),
+    )
+
+
+# ---------------------------------------------------------------------------
+# Decode.  codes(): Eq. (8), pinned by Figure 1, the prefix property and the
+# closed-form code.  w_main(): Eq. (9), pinned by Eq. (10) (exhaustive, exact
+# rationals), the midpoint property (Appendix C, Eq. 12), the error bound t_M,
+# the reach rho (Eq. 6) and the textbook INT2 special case.
+# ---------------------------------------------------------------------------
+def _check_bits(F: Fields, M: int):
+    if not (2 <= M <= F.nbits):
+        raise ValueError(f"bits must be in [2, {F.nbits}]")
+
+
+def codes(F: Fields, M: int) -> np.ndarray:
+    """Composite integer u_M = q 2^(M-2) + sum_{k=3..M} b_k 2^(M-k) (Eq. 8), uint8 [R, C]."""
+    _check_bits(F, M)
+    u = F.q.astype(np.int64) << (M - 2)
+    for k in range(3, M + 1):
+        u += F.planes[k - 3].astype(np.int64) << (M - k)
+    return u.astype(np.uint8)
+
+
+def _expand(F: Fields, a: np.ndarray) -> np.ndarray:
+    return np.repeat(a.astype(np.float64), F.group, axis=1)
+
+
+def w_main(F: Fields, M: int, rows: Optional[slice] = None) -> np.ndarray:
+    """Main-stream reconstruction lo + s q + sum (2 b_k - 1) s/2^(k-1) (Eq. 9), float64."""
+    _check_bits(F, M)
+    sl = rows if rows is not None else slice(None)
+    lo = _expand(F, F.lo[sl])
+    s = _expand(F, F.s[sl])
+    w = lo + s * F.q[sl].astype(np.float64)
+    for k in range(3, M + 1):
+        w += (2.0 * F.planes[k - 3][sl].astype(np.float64) - 1.0) * s / 2.0 ** (k - 1)
+    return w
+
+
+def w_hat(F: Fields, M: int, rows: Optional[slice] = None) -> np.ndarray:
+    """Complete reconstruction (1 - m) W_main + P (Eq. 4), float64."""
+    sl = rows if rows is not None else slice(None)
+    wm = w_main(F, M, sl)
+    m = F.mask[sl]
+    start = 0 if sl.start is None else sl.start
+    stop = F.rows if sl.stop is None else sl.stop
+    P = np.zeros_like(wm)
+    lo_e, hi_e = int(F.row_ptr[start]), int(F.row_ptr[stop])
+    rr = np.repeat(np.arange(start, stop), np.diff(F.row_ptr[start:stop + 1]))
+    P[rr - start, F.col[lo_e:hi_e]] = F.val[lo_e:hi_e].astype(np.float64)
+    return np.where(m, P, wm)
+
+
+def gemv(F: Fields, x16: np.ndarray, M: int, block_rows: int = 8192) -> np.ndarray:
+    """y = W_hat^(M) x in float64 (streams row blocks to bound memory)."""
+    x = np.asarray(x16).astype(np.float64)
+    if x.shape != (F.cols,):
+        raise ValueError("x must have shape [cols]")
+    y = np.empty(F.rows, dtype=np.float64)
+    for r0 in range(0, F.rows, block_rows):
+        r1 = min(F.rows, r0 + block_rows)
+        y[r0:r1] = w_hat(F, M, slice(r0, r1)) @ x
+    return y
