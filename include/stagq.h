@@ -1,0 +1,196 @@
+/*
+ * stagq.h -- C ABI of the StagQ batch-one GEMV library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * StagQ ("StagQ: Constraint-Driven Multi-Precision Weight Quantization for
+ * LLMs") stores a weight matrix once as a multi-precision main stream plus a
+ * sparse side record:
+ *   - a 2-bit group-wise affine base code q in {0..3} (section 3.3),
+ *   - 1-bit refinement planes b_k, k = 3..N, each the sign of the residual
+ *     left by the preceding prefix, on the dyadic half-step schedule
+ *     t_k = s / 2^(k-1) (section 3.2, Eq. 7),
+ *   - one (lo, s) pair per group of g consecutive input columns, shared by
+ *     every precision (section 3.1),
+ *   - a side record P of held-out weights (section 3, Eq. 4).
+ * A read at precision M (2 <= M <= N) decodes the composite integer
+ * u_M = q 2^(M-2) + sum_{k=3..M} b_k 2^(M-k) (Eq. 8) through one affine map,
+ * W_main = lo_M + s_M u_M with s_M = s / 2^(M-2) and
+ * lo_M = lo - s (2^(M-2) - 1) / 2^(M-1) (section 3.4, Eq. 10), and the complete
+ * reconstruction is (1 - m) * W_main + P (Eq. 4).
+ *
+ * Matrices are rows (output channels) x cols (input channels); a group is g
+ * consecutive columns of one row.  Supported: cols a positive multiple of 128,
+ * g in {32, 64, 128}, 2 <= N <= 8, every device stream below 2 GiB.
+ *
+ * Conventions for every call:
+ *   - Return value: STAGQ_OK (0) or a negative STAGQ_E* status.  Arguments are
+ *     validated on the host before anything is launched; no C++ exception
+ *     crosses this interface.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are HIP device
+ *     memory on the current device.  A hip_stream of NULL means the default
+ *     stream.
+ *   - fp16 values are passed as their IEEE binary16 bit patterns (uint16_t).
+ */
+#ifndef STAGQ_H
+#define STAGQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define STAGQ_OK       0
+#define STAGQ_EINVAL  (-1)  /* null pointer, zero size where one is needed, bad argument */
+#define STAGQ_EBITS   (-2)  /* bits outside [2, N] */
+#define STAGQ_ESHAPE  (-3)  /* unsupported rows/cols/group/N, or a stream >= 2 GiB */
+#define STAGQ_ECSR    (-4)  /* malformed side record (row_ptr, col order/range) */
+#define STAGQ_EALIGN  (-5)  /* pointer not aligned as documented */
+#define STAGQ_EHIP    (-6)  /* a HIP runtime call failed */
+#define STAGQ_EFIELD  (-7)  /* field out of range: q > 3, plane bit > 1, plane bit set at a
+                               held-out position, non-finite lo or s */
+#define STAGQ_ESIZE   (-8)  /* destination buffer too small / image size mismatch */
+#define STAGQ_EIMAGE  (-9)  /* packed image header not recognised */
+
+typedef struct stagq_handle_s* stagq_handle;
+
+/*
+ * Unpacked encoder output in host memory, caller-owned, read during the call
+ * only.  Layouts are row-major.
+ *   q        [rows*cols]                 base codes 0..3
+ *   planes   [(N-2)*rows*cols]           refinement bits 0/1, plane k = 3 first
+ *   lo, s    [rows*(cols/group)]         fp16 bits of the group pair
+ *   row_ptr  [rows+1], col [nnz], val [nnz]: the side record P as CSR sorted by
+ *            (row, col); val holds the fp16 bits of the recorded weight.
+ * The planes must be 0 at held-out positions (section 3.6: the planes skip every
+ * position the side record carries); q there is the base code of the original
+ * weight.
+ */
+typedef struct {
+  int32_t rows, cols, group, nbits_max;
+  const uint8_t* q;
+  const uint8_t* planes;
+  const uint16_t* lo;
+  const uint16_t* s;
+  const int32_t* row_ptr;
+  const int32_t* col;
+  const uint16_t* val;
+  int64_t nnz;
+} stagq_fields;
+
+/* Shape and traffic of a packed matrix. */
+typedef struct {
+  int32_t rows, cols, group, nbits_max;
+  int64_t nnz;
+  uint64_t image_bytes;      /* size of the packed image */
+  /* Algorithmic bytes one GEMV at precision b moves, for b = 2..N (index b;
+   * 0 elsewhere): base stream + planes 3..b + group pairs + side record
+   * (row_ptr, col/q words, values) + x (fp16) + y (fp32). */
+  uint64_t bytes_read[9];
+} stagq_info;
+
+/* Bytes of the packed image for these fields (0 if the shape is unsupported). */
+size_t stagq_packed_bytes(const stagq_fields* f);
+
+/*
+ * Validate f and write its packed image into host memory dst (dst_bytes >=
+ * stagq_packed_bytes(f), 16-byte aligned).  Pure host code: no HIP call.  The
+ * image is plane-major: the base stream, then plane 3, 4, ..., N, then the group
+ * pairs and the side record, so a read at precision M touches only the base and
+ * planes 3..M (section 3.3: fields stored in plane order).
+ */
+int stagq_pack_host(const stagq_fields* f, void* dst, size_t dst_bytes);
+
+/*
+ * Validate f, build the packed image and copy it into caller-owned device
+ * memory dev_buf (dev_bytes >= stagq_packed_bytes(f), 256-byte aligned), on
+ * hip_stream; returns once the copy has completed (the call synchronises
+ * hip_stream).  *out receives a new handle: a host-side descriptor that refers
+ * to dev_buf without owning it.  dev_buf must outlive the handle.
+ */
+int stagq_pack(const stagq_fields* f, void* dev_buf, size_t dev_bytes, void* hip_stream,
+               stagq_handle* out);
+
+/*
+ * New handle for another device buffer that already holds a byte-identical copy
+ * of the image behind h (for instance several copies for cache-cold timing).
+ * dev_buf is 256-byte aligned and at least the image size; not owned.
+ */
+int stagq_rebind(stagq_handle h, void* dev_buf, size_t dev_bytes, stagq_handle* out);
+
+/*
+ * y = W_hat^(bits) x (Eq. 4 with Eq. 10), batch one.
+ *   x    device, fp16 [cols], 16-byte aligned
+ *   y    device, fp32 [rows], 4-byte aligned (written, not accumulated)
+ *        (with rows == 0 the call does nothing and x, y may be NULL)
+ *   bits precision M of this call, 2 <= bits <= N; any call may pick any M on
+ *        the same handle (one stream serves every precision).
+ * One kernel launch on hip_stream; asynchronous (no synchronisation), no
+ * allocation.  The result is deterministic for a given shape and bits (fixed
+ * summation order, no atomics).  Handles are immutable, so calls on different
+ * streams may run concurrently.
+ */
+int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stream);
+
+/*
+ * Write the composite integers u_bits (Eq. 8) of the main stream as decoded by
+ * the GEMV path: codes is device uint8 [rows*cols], row-major, 16-byte aligned.
+ * Asynchronous on hip_stream.  (Held-out positions decode like any other: q
+ * followed by zero planes.)
+ */
+int stagq_decode_codes(stagq_handle h, int bits, uint8_t* codes, void* hip_stream);
+
+/*
+ * Launch shape the GEMV uses for a matrix of this shape at precision bits (on
+ * the current device, or assuming 256 compute units when none is present):
+ * out[0] workgroups, out[1] threads per workgroup, out[2] rows per pass,
+ * out[3] passes, out[4] rows per workgroup, out[5] LDS bytes, out[6] lanes per
+ * row in the final reduction, out[7] passes of loads in flight.  out is host
+ * int32[8].  Pure host logic.
+ */
+int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int bits,
+                    int32_t* out);
+
+/* Fill *out with shape and per-precision traffic of h. */
+int stagq_query(stagq_handle h, stagq_info* out);
+
+/* Release the host descriptor (never frees device memory).  NULL is a no-op. */
+void stagq_destroy(stagq_handle h);
+
+/* Static description of a status code. */
+const char* stagq_strerror(int status);
+
+/*
+ * Reference-grade encoder of the library (host, multi-threaded), following the
+ * encoder of section 3.6 / Appendix E without calibration data: ratio-criterion
+ * pre-grid guard (at most one entry per group whose magnitude exceeds ratio_T
+ * times the group's second largest, ranked by that ratio), min-max pair fit over
+ * the remaining entries stored as fp16, nearest base code (ties upward),
+ * post-grid guard on the largest two-bit residuals of the matrix, and planes
+ * that store the sign of the residual of the preceding prefix (sign(0) = +1),
+ * skipping held-out positions.  budget is the side-record size K.
+ *   w       host fp16 [rows*cols]
+ *   outputs host, caller-allocated: q [rows*cols], planes [(N-2)*rows*cols],
+ *           lo, s [rows*cols/group], row_ptr [rows+1], col [budget], val [budget];
+ *           *n_pre receives how many entries the pre-grid guard took.
+ * group may be any divisor of cols here (packing restricts it further).
+ */
+int stagq_encode(const uint16_t* w, int32_t rows, int32_t cols, int32_t group, int32_t nbits,
+                 int64_t budget, double ratio_T, uint8_t* q, uint8_t* planes, uint16_t* lo,
+                 uint16_t* s, int32_t* row_ptr, int32_t* col, uint16_t* val, int64_t* n_pre);
+
+/*
+ * Inverse of stagq_pack_host for a host copy of an image (layout round-trip
+ * checks): writes the fields into caller-allocated host arrays sized as in
+ * stagq_fields (the shape is read from the image header into *shape).
+ */
+int stagq_unpack_host(const void* image, size_t image_bytes, stagq_info* shape, uint8_t* q,
+                      uint8_t* planes, uint16_t* lo, uint16_t* s, int32_t* row_ptr, int32_t* col,
+                      uint16_t* val);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STAGQ_H */

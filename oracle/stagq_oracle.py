@@ -188,10 +188,17 @@ def encode(w16: np.ndarray, group: int, nbits: int, frac: float, T: float = 4.0)
     r2 = np.abs(wg - (lo_f + s_f * q))
     n_post = K - n_pre
     if n_post > 0:
-        free_flat = flat[~mask]
+        free_flat = flat[~mask]                     # ascending flat index
         free_r2 = r2[~mask]
-        order = np.lexsort((free_flat, -free_r2))
-        pick = free_flat[order[:n_post]]
+        if n_post >= free_r2.shape[0]:
+            pick = free_flat
+        else:
+            # the n_post-th largest residual; everything above it is taken, and
+            # the entries equal to it are taken in flat-index order
+            kth = np.partition(free_r2, free_r2.shape[0] - n_post)[free_r2.shape[0] - n_post]
+            above = free_r2 > kth
+            ties = np.nonzero(free_r2 == kth)[0][: n_post - int(above.sum())]
+            pick = np.concatenate([free_flat[above], free_flat[ties]])
         mask.reshape(-1)[pick] = True
 
     # 5. Planes: sign of the residual of the preceding prefix (sections 3.3, 3.6);

@@ -1,0 +1,181 @@
+"""StagQ multi-precision weight-only batch-one GEMV for AMD MI355X (gfx950).
+
+Python face of libstagq.so (C ABI in include/stagq.h).  The functions here only
+marshal arguments; packing, decoding and the GEMV run in the native library.
+
+    import precision_weight_only_amd as pwo
+    fields = pwo.encode(w_fp16, group=128, nbits=4, budget=K)      # host encoder
+    m = pwo.StagQMatrix.pack(fields, device="cuda:0")               # plane-major image in HBM
+    y = m.gemv(x_fp16_cuda, bits=3)                                 # precision chosen per call
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import _lib as _lib_mod
+from ._lib import EXPORTED, Info, StagQError, check, fields_struct, lib  # noqa: F401
+
+
+def load() -> None:
+    """Load libstagq.so now (raises ImportError if it has not been built)."""
+    lib()
+
+__all__ = ["StagQMatrix", "encode", "pack_host", "unpack_host", "packed_bytes", "plan_gemv",
+           "StagQError"]
+
+
+def _torch():
+    import torch  # PyTorch only provides device memory and streams
+    return torch
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def encode(w16: np.ndarray, group: int, nbits: int, budget: int, ratio_T: float = 4.0) -> Dict:
+    """Run the library's host encoder on an fp16 matrix; returns the unpacked fields."""
+    w = np.ascontiguousarray(w16, dtype=np.float16)
+    R, Cc = w.shape
+    G = Cc // group
+    out = dict(
+        q=np.empty((R, Cc), np.uint8), planes=np.empty((nbits - 2, R, Cc), np.uint8),
+        lo=np.empty((R, G), np.float16), s=np.empty((R, G), np.float16),
+        row_ptr=np.empty(R + 1, np.int32), col=np.empty(budget, np.int32),
+        val=np.empty(budget, np.float16))
+    n_pre = C.c_int64(0)
+    p = lambda a: a.ctypes.data_as(C.c_void_p)
+    st = lib().stagq_encode(p(w), R, Cc, group, nbits, budget, float(ratio_T), p(out["q"]),
+                            p(out["planes"]) if nbits > 2 else None, p(out["lo"]), p(out["s"]),
+                            p(out["row_ptr"]), p(out["col"]) if budget else None,
+                            p(out["val"]) if budget else None, C.byref(n_pre))
+    check(st, "stagq_encode")
+    out.update(group=group, nbits=nbits, n_pre=int(n_pre.value))
+    return out
+
+
+def plan_gemv(rows: int, cols: int, group: int, nbits: int, bits: int) -> Dict[str, int]:
+    """Launch shape the library picks for this GEMV (workgroups, threads, ...)."""
+    out = (C.c_int32 * 8)()
+    check(lib().stagq_plan_gemv(rows, cols, group, nbits, bits, C.cast(out, C.c_void_p)),
+          "stagq_plan_gemv")
+    keys = ("grid", "threads", "rows_per_pass", "passes", "rows_per_group", "lds_bytes",
+            "lanes_per_row", "depth")
+    return dict(zip(keys, list(out)))
+
+
+def packed_bytes(fields) -> int:
+    keep: list = []
+    return int(lib().stagq_packed_bytes(C.byref(fields_struct(fields, keep))))
+
+
+def pack_host(fields) -> np.ndarray:
+    """Packed image in host memory (uint8 array)."""
+    keep: list = []
+    fs = fields_struct(fields, keep)
+    n = int(lib().stagq_packed_bytes(C.byref(fs)))
+    if n == 0:
+        check(-3, "stagq_packed_bytes")
+    img = np.zeros(n, dtype=np.uint8)
+    check(lib().stagq_pack_host(C.byref(fs), img.ctypes.data_as(C.c_void_p), n), "stagq_pack_host")
+    return img
+
+
+def unpack_host(image: np.ndarray) -> Dict:
+    """Inverse of pack_host (layout round trip)."""
+    image = np.ascontiguousarray(image, dtype=np.uint8)
+    info = Info()
+    check(lib().stagq_unpack_host(image.ctypes.data_as(C.c_void_p), image.size, C.byref(info),
+                                  None, None, None, None, None, None, None), "stagq_unpack_host")
+    R, Cc, g, N, nnz = info.rows, info.cols, info.group, info.nbits_max, info.nnz
+    out = dict(q=np.empty((R, Cc), np.uint8), planes=np.empty((N - 2, R, Cc), np.uint8),
+               lo=np.empty((R, Cc // g), np.uint16), s=np.empty((R, Cc // g), np.uint16),
+               row_ptr=np.empty(R + 1, np.int32), col=np.empty(nnz, np.int32),
+               val=np.empty(nnz, np.uint16))
+    p = lambda a: a.ctypes.data_as(C.c_void_p) if a.size else None
+    check(lib().stagq_unpack_host(image.ctypes.data_as(C.c_void_p), image.size, C.byref(info),
+                                  p(out["q"]), p(out["planes"]), p(out["lo"]), p(out["s"]),
+                                  p(out["row_ptr"]), p(out["col"]), p(out["val"])), "stagq_unpack_host")
+    out["lo"] = out["lo"].view(np.float16)
+    out["s"] = out["s"].view(np.float16)
+    out["val"] = out["val"].view(np.float16)
+    out.update(rows=R, cols=Cc, group=g, nbits=N, nnz=nnz)
+    return out
+
+
+class StagQMatrix:
+    """A packed StagQ matrix resident in device memory (one image, every precision)."""
+
+    def __init__(self, handle: C.c_void_p, buffer, info: Info):
+        self._h = handle
+        self.buffer = buffer          # torch uint8 tensor holding the image (kept alive)
+        self.rows, self.cols = info.rows, info.cols
+        self.group, self.nbits = info.group, info.nbits_max
+        self.nnz = info.nnz
+        self.image_bytes = info.image_bytes
+        self.bytes_read = {b: int(info.bytes_read[b]) for b in range(2, self.nbits + 1)}
+
+    @classmethod
+    def pack(cls, fields, device="cuda:0", stream=None) -> "StagQMatrix":
+        torch = _torch()
+        keep: list = []
+        fs = fields_struct(fields, keep)
+        n = int(lib().stagq_packed_bytes(C.byref(fs)))
+        if n == 0:
+            check(-3, "stagq_packed_bytes")
+        buf = torch.empty(n, dtype=torch.uint8, device=device)
+        h = C.c_void_p()
+        with torch.cuda.device(buf.device):
+            check(lib().stagq_pack(C.byref(fs), C.c_void_p(buf.data_ptr()), n, _stream_ptr(stream),
+                                   C.byref(h)), "stagq_pack")
+        info = Info()
+        check(lib().stagq_query(h, C.byref(info)), "stagq_query")
+        return cls(h, buf, info)
+
+    def clone_to(self, buffer) -> "StagQMatrix":
+        """Handle for another device buffer holding a copy of this image."""
+        h = C.c_void_p()
+        check(lib().stagq_rebind(self._h, C.c_void_p(buffer.data_ptr()), buffer.numel(), C.byref(h)),
+              "stagq_rebind")
+        info = Info()
+        check(lib().stagq_query(h, C.byref(info)), "stagq_query")
+        return StagQMatrix(h, buffer, info)
+
+    def replicate(self) -> "StagQMatrix":
+        torch = _torch()
+        buf = torch.empty_like(self.buffer)
+        buf.copy_(self.buffer)
+        return self.clone_to(buf)
+
+    def gemv(self, x, bits: int, y=None, stream=None):
+        """y = W_hat^(bits) x for an fp16 device vector x; returns fp32 y."""
+        torch = _torch()
+        if y is None:
+            y = torch.empty(self.rows, dtype=torch.float32, device=x.device)
+        check(lib().stagq_gemv(self._h, C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()),
+                               int(bits), _stream_ptr(stream)), "stagq_gemv")
+        return y
+
+    def gemv_raw(self, x_ptr: int, y_ptr: int, bits: int, stream_ptr) -> int:
+        """Launch with raw device pointers; returns the status (no checking)."""
+        return lib().stagq_gemv(self._h, C.c_void_p(x_ptr), C.c_void_p(y_ptr), int(bits), stream_ptr)
+
+    def decode_codes(self, bits: int, out=None, stream=None):
+        torch = _torch()
+        if out is None:
+            out = torch.empty((self.rows, self.cols), dtype=torch.uint8, device=self.buffer.device)
+        check(lib().stagq_decode_codes(self._h, int(bits), C.c_void_p(out.data_ptr()),
+                                       _stream_ptr(stream)), "stagq_decode_codes")
+        return out
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib_mod._lib is not None:
+            _lib_mod._lib.stagq_destroy(h)
+            self._h = None

@@ -1,0 +1,797 @@
+// Device half of the StagQ library for gfx950 (MI355X): the decode-fused
+// batch-one GEMV, the code-dump kernel, and their host dispatch.
+//
+// GEMV design (one launch per call):
+//  * A lane owns one 128-column tile of one row.  A workgroup of k waves runs
+//    `rpp` rows side by side (rpp * tiles_per_row <= 64k lanes) for NP passes,
+//    so it owns RB = NP * rpp consecutive rows and a contiguous range of every
+//    stream.  All global loads go through buffer resources: out-of-range lanes
+//    read zeros instead of faulting.
+//  * x (fp16) is staged once into LDS, then each lane keeps the 128 values of
+//    its tile in 64 VGPRs as fp16 pairs, permuted to match the bit placement of
+//    the packed stream (see stagq_layout.h).
+//  * Per pass a lane fetches its tile's base stream (2 x dwordx4), planes 3..M
+//    (1 x dwordx4 each) and group pairs, D passes ahead of use.
+//  * Decode: the codes of two weights are isolated into the low mantissa bits
+//    of the two fp16 halves of a register (fp16 subnormals, value u * 2^-24,
+//    exact), so one v_dot2_f32_f16 multiplies two codes by two x values and
+//    accumulates in fp32.  For M >= 3 the planes are first merged with the base
+//    codes into 4-bit codes (Eq. 8) with shifts and bit-field inserts.
+//  * Per tile and group: partial = s_M * sum(u x) + lo_M * sum(x) (the affine
+//    collapse of Eq. 10 summed over the group), in fp32.
+//  * Side record (Eq. 4): each entry contributes (P - W_main) x_c, where the
+//    main stream decodes W_main = lo + s (q - 1/2 + 2^(1-M)) there because its
+//    planes are zero.  Entries are prefetched in the prologue and corrected at
+//    the end from LDS copies of the group pairs and x.
+//  * Row sums: fixed-order sums of the tile partials and the row's corrections
+//    (no atomics), so y is bitwise reproducible for a given shape and M.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+
+#include "stagq_internal.h"
+
+namespace stagq {
+namespace dev {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr uint32_t kOOB = 0x80000000u;  // offset past every stream (< 2 GiB each)
+constexpr int kXChunks = 8;             // x staging: up to 8 dwordx4 per thread
+constexpr int kEntries = 4;             // side-record entries prefetched per thread
+constexpr uint32_t kOneOne = 0x3C003C00u;  // fp16 pair (1.0, 1.0)
+
+__device__ __forceinline__ rsrc_t mk(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ld128(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 ld64(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c, false);
+}
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
+  return (a & m) | (b & ~m);
+}
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+// fp16 pair (x[a], x[b]) from raw pairs xr[i] = (x[2i], x[2i+1]).
+__device__ __forceinline__ uint32_t pick(const uint32_t* xr, int a, int b) {
+  const uint32_t lo = (xr[a >> 1] >> ((a & 1) * 16)) & 0xffffu;
+  const uint32_t hi = (xr[b >> 1] >> ((b & 1) * 16)) & 0xffffu;
+  return lo | (hi << 16);
+}
+
+// 2-bit fields (hi plane bit, lo plane bit) for the even / odd columns of a
+// 32-column block, aligned with the base-stream dwords 2d / 2d+1.
+__device__ __forceinline__ void pair_fields(uint32_t phi, uint32_t plo, uint32_t& ev, uint32_t& od) {
+  ev = bfi(0x55555555u, plo, phi << 1);
+  od = bfi(0xAAAAAAAAu, phi, plo >> 1);
+}
+// 4-bit codes from a high 2-bit field word and a low 2-bit field word:
+// nibble m of zlo / zhi is the code of field 2m / 2m+1.
+__device__ __forceinline__ void nibbles(uint32_t hw, uint32_t lw, uint32_t& zlo, uint32_t& zhi) {
+  zlo = bfi(0x33333333u, lw, hw << 2);
+  zhi = bfi(0xCCCCCCCCu, hw, lw >> 2);
+}
+
+struct GemvParams {
+  const uint8_t* s0;       // base stream, chunk 0 (chunk 1 follows at +chunk_bytes)
+  const uint8_t* planes;   // plane 3 (plane k at +(k-3)*chunk_bytes)
+  const uint8_t* meta;
+  const uint8_t* row_ptr;
+  const uint8_t* colq;
+  const uint8_t* val;
+  const uint8_t* x;
+  float* y;
+  uint32_t chunk_bytes, meta_bytes, colq_bytes, val_bytes, rp_bytes, x_bytes;
+  int32_t R, C, T, g, rpp, P, NP, RB, L;
+  uint32_t lds_rp, lds_meta, lds_part, lds_corr, lds_rowcorr;
+};
+
+template <int M, int GU>
+struct Slot {
+  u32x4 a, b;                        // base stream: dwords 0..3, 4..7
+  u32x4 pl[M > 2 ? M - 2 : 1];       // planes 3..M, dwords 0..3
+  uint32_t meta[GU];                 // (lo | s << 16) of the tile's groups
+};
+
+template <int M, int GU>
+__device__ __forceinline__ void issue(Slot<M, GU>& s, const rsrc_t& rA, const rsrc_t& rB,
+                                      const rsrc_t* rP, const rsrc_t& rMeta, uint32_t tile, bool ok) {
+  const uint32_t off = ok ? tile * 16u : kOOB;
+  s.a = ld128(rA, off);
+  s.b = ld128(rB, off);
+#pragma unroll
+  for (int k = 0; k < M - 2; k++) s.pl[k] = ld128(rP[k], off);
+  const uint32_t offm = ok ? tile * (4u * GU) : kOOB;
+  if constexpr (GU == 1) {
+    s.meta[0] = ld32(rMeta, offm);
+  } else if constexpr (GU == 2) {
+    u32x2 v = ld64(rMeta, offm);
+    s.meta[0] = v[0]; s.meta[1] = v[1];
+  } else {
+    u32x4 v = ld128(rMeta, offm);
+    s.meta[0] = v[0]; s.meta[1] = v[1]; s.meta[2] = v[2]; s.meta[3] = v[3];
+  }
+}
+
+__device__ __forceinline__ uint32_t s0_dword(const u32x4& a, const u32x4& b, int dw) {
+  return dw < 4 ? a[dw] : b[dw - 4];
+}
+
+// sum over the tile of (s_M u_M + lo_M) x, i.e. Eq. 10 summed per group.
+template <int M, int GU>
+__device__ __forceinline__ float tile_partial(const Slot<M, GU>& s, const uint32_t* xp, const float* sx) {
+  constexpr float kM = float((1 << (M - 2)) - 1) / float(1 << (M - 1));  // (2^(M-2)-1)/2^(M-1)
+  float sum[GU];
+  if constexpr (M == 2) {
+    float acc[GU][5];
+#pragma unroll
+    for (int gi = 0; gi < GU; gi++)
+#pragma unroll
+      for (int i = 0; i < 5; i++) acc[gi][i] = 0.f;
+#pragma unroll
+    for (int dw = 0; dw < 8; dw++) {
+      const int gi = (dw >> 1) * GU / 4;
+      const uint32_t w = s0_dword(s.a, s.b, dw);
+      const uint32_t* xq = xp + dw * 8;
+      acc[gi][0] = dot2(w & 0x00030003u, xq[0], acc[gi][0]);
+      acc[gi][1] = dot2(w & 0x000C000Cu, xq[1], acc[gi][1]);
+      acc[gi][2] = dot2(w & 0x00300030u, xq[2], acc[gi][2]);
+      acc[gi][3] = dot2(w & 0x00C000C0u, xq[3], acc[gi][3]);
+      acc[gi][4] = dot2(w & 0x03000300u, xq[4], acc[gi][4]);
+      const uint32_t t = w >> 6;
+      acc[gi][2] = dot2(t & 0x00300030u, xq[5], acc[gi][2]);
+      acc[gi][3] = dot2(t & 0x00C000C0u, xq[6], acc[gi][3]);
+      acc[gi][4] = dot2(t & 0x03000300u, xq[7], acc[gi][4]);
+    }
+#pragma unroll
+    for (int gi = 0; gi < GU; gi++)
+      sum[gi] = acc[gi][0] * 0x1p24f + acc[gi][1] * 0x1p22f + acc[gi][2] * 0x1p20f +
+                acc[gi][3] * 0x1p18f + acc[gi][4] * 0x1p16f;
+  } else {
+    float aA[GU], aB[GU], aC[GU];
+#pragma unroll
+    for (int gi = 0; gi < GU; gi++) { aA[gi] = 0.f; aB[gi] = 0.f; aC[gi] = 0.f; }
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      const int gi = d * GU / 4;
+      uint32_t ye, yo;
+      const uint32_t p3 = s.pl[0][d];
+      if constexpr (M >= 4) {
+        pair_fields(p3, s.pl[1][d], ye, yo);
+      } else {
+        ye = (p3 << 1) & 0xAAAAAAAAu;
+        yo = p3 & 0xAAAAAAAAu;
+      }
+      uint32_t ve = 0, vo = 0, we = 0, wo = 0;
+      if constexpr (M >= 5) {
+        const uint32_t p5 = s.pl[2][d];
+        if constexpr (M >= 6) {
+          pair_fields(p5, s.pl[3][d], ve, vo);
+        } else {
+          ve = (p5 << 1) & 0xAAAAAAAAu;
+          vo = p5 & 0xAAAAAAAAu;
+        }
+        if constexpr (M >= 7) {
+          const uint32_t p7 = s.pl[4][d];
+          if constexpr (M >= 8) {
+            pair_fields(p7, s.pl[5][d], we, wo);
+          } else {
+            we = (p7 << 1) & 0xAAAAAAAAu;
+            wo = p7 & 0xAAAAAAAAu;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 2; e++) {
+        uint32_t z[2];
+        nibbles(s0_dword(s.a, s.b, 2 * d + e), e ? yo : ye, z[0], z[1]);
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          const uint32_t* xq = xp + ((d * 2 + e) * 2 + h) * 4;
+          const uint32_t zz = z[h], t = zz >> 8;
+          aA[gi] = dot2(zz & 0x000F000Fu, xq[0], aA[gi]);
+          aB[gi] = dot2(zz & 0x00F000F0u, xq[1], aB[gi]);
+          aA[gi] = dot2(t & 0x000F000Fu, xq[2], aA[gi]);
+          aB[gi] = dot2(t & 0x00F000F0u, xq[3], aB[gi]);
+        }
+        if constexpr (M >= 5) {
+          uint32_t v[2];
+          nibbles(e ? vo : ve, e ? wo : we, v[0], v[1]);
+#pragma unroll
+          for (int h = 0; h < 2; h++) {
+            const uint32_t* xq = xp + ((d * 2 + e) * 2 + h) * 4;
+            const uint32_t zz = v[h], t = zz >> 8;
+            aB[gi] = dot2(zz & 0x000F000Fu, xq[0], aB[gi]);
+            aC[gi] = dot2(zz & 0x00F000F0u, xq[1], aC[gi]);
+            aB[gi] = dot2(t & 0x000F000Fu, xq[2], aB[gi]);
+            aC[gi] = dot2(t & 0x00F000F0u, xq[3], aC[gi]);
+          }
+        }
+      }
+    }
+    // s_M sum(u_M x) = s * (aA 2^22 + aB 2^18 + aC 2^14) for every M >= 3.
+#pragma unroll
+    for (int gi = 0; gi < GU; gi++)
+      sum[gi] = aA[gi] * 0x1p22f + aB[gi] * 0x1p18f + (M >= 5 ? aC[gi] * 0x1p14f : 0.f);
+  }
+  float part = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < GU; gi++) {
+    const float lo = h2f(s.meta[gi] & 0xffffu), st = h2f(s.meta[gi] >> 16);
+    part += st * (sum[gi] - kM * sx[gi]) + lo * sx[gi];
+  }
+  return part;
+}
+
+template <int M, int GU, int D>
+__global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
+  int32_t* rp = reinterpret_cast<int32_t*>(lds + p.lds_rp);
+  uint32_t* meta_s = reinterpret_cast<uint32_t*>(lds + p.lds_meta);
+  float* part_s = reinterpret_cast<float*>(lds + p.lds_part);
+  float* corr_s = reinterpret_cast<float*>(lds + p.lds_corr);
+  float* rowcorr_s = reinterpret_cast<float*>(lds + p.lds_rowcorr);
+
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int r0 = blockIdx.x * p.RB;
+  const int rip = tid / p.T;            // row slot within a pass
+  const int t = tid - rip * p.T;        // tile column
+  const bool act = rip < p.rpp;
+
+  const rsrc_t rA = mk(p.s0, p.chunk_bytes);
+  const rsrc_t rB = mk(p.s0 + p.chunk_bytes, p.chunk_bytes);
+  rsrc_t rP[M > 2 ? M - 2 : 1];
+#pragma unroll
+  for (int k = 0; k < M - 2; k++) rP[k] = mk(p.planes + uint64_t(k) * p.chunk_bytes, p.chunk_bytes);
+  const rsrc_t rMeta = mk(p.meta, p.meta_bytes);
+  const rsrc_t rX = mk(p.x, p.x_bytes);
+  const rsrc_t rRp = mk(p.row_ptr, p.rp_bytes);
+  const rsrc_t rCq = mk(p.colq, p.colq_bytes);
+  const rsrc_t rVal = mk(p.val, p.val_bytes);
+
+  // --- prologue: x and row_ptr first, then the first D passes of weights.
+  const int xchunks = p.C >> 3;
+  u32x4 xv[kXChunks];
+#pragma unroll
+  for (int i = 0; i < kXChunks; i++) {
+    const int ci = tid + i * nthr;
+    xv[i] = ld128(rX, ci < xchunks ? uint32_t(ci) * 16u : kOOB);
+  }
+  uint32_t rpv[2];  // row_ptr[r0 .. r0 + RB], clamped at R (RB + 1 <= 2 * nthr)
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int j = tid + i * nthr;
+    rpv[i] = ld32(rRp, j <= p.RB ? uint32_t(min(r0 + j, p.R)) * 4u : kOOB);
+  }
+
+  Slot<M, GU> sl[D];
+#pragma unroll
+  for (int i = 0; i < D; i++) {
+    const int row = r0 + i * p.rpp + rip;
+    issue(sl[i], rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && i < p.NP && row < p.R);
+  }
+
+#pragma unroll
+  for (int i = 0; i < kXChunks; i++) {
+    const int ci = tid + i * nthr;
+    if (ci < xchunks) *reinterpret_cast<u32x4*>(xs + ci * 8) = xv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+    if (tid + i * nthr <= p.RB) rp[tid + i * nthr] = int32_t(rpv[i]);
+  for (int i = tid; i < p.RB; i += nthr) rowcorr_s[i] = 0.f;
+  __syncthreads();
+
+  // --- side record: prefetch this workgroup's first entries, find their rows.
+  const int e0 = rp[0], e1 = rp[p.RB];
+  uint32_t cq[kEntries], pv[kEntries];
+  int erow[kEntries];
+#pragma unroll
+  for (int j = 0; j < kEntries; j++) {
+    const int e = e0 + tid + j * nthr;
+    const bool ok = e < e1;
+    cq[j] = ld32(rCq, ok ? uint32_t(e) * 4u : kOOB);
+    pv[j] = ld16(rVal, ok ? uint32_t(e) * 2u : kOOB);
+    int lo = 0, hi = p.RB;           // rp[lo] <= e < rp[hi]
+    if (ok) {
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (rp[mid] <= e) lo = mid; else hi = mid;
+      }
+    }
+    erow[j] = lo;
+  }
+
+  // --- x slice of this lane's tile as permuted fp16 pairs; per-group sum(x).
+  uint32_t xp[64];
+  float sx[GU];
+#pragma unroll
+  for (int gi = 0; gi < GU; gi++) sx[gi] = 0.f;
+  const uint16_t* xt = xs + (act ? t : 0) * 128;
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    uint32_t xr[64];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xt + 32 * d + 8 * q4);
+      xr[16 * d + 4 * q4 + 0] = v[0]; xr[16 * d + 4 * q4 + 1] = v[1];
+      xr[16 * d + 4 * q4 + 2] = v[2]; xr[16 * d + 4 * q4 + 3] = v[3];
+    }
+    const int gi = d * GU / 4;
+#pragma unroll
+    for (int i = 0; i < 16; i++) sx[gi] = dot2(xr[16 * d + i], kOneOne, sx[gi]);
+    if constexpr (M == 2) {
+#pragma unroll
+      for (int e = 0; e < 2; e++)
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          xp[(2 * d + e) * 8 + i] = pick(xr, 32 * d + 2 * i + e, 32 * d + 16 + 2 * i + e);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 2; e++)
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+          for (int m = 0; m < 4; m++)
+            xp[((d * 2 + e) * 2 + h) * 4 + m] =
+                pick(xr, 32 * d + 4 * m + 2 * h + e, 32 * d + 16 + 4 * m + 2 * h + e);
+    }
+  }
+
+  // --- main loop over passes, D passes of loads in flight.
+  for (int pb = 0; pb < p.NP; pb += D) {
+#pragma unroll
+    for (int i = 0; i < D; i++) {
+      const int pass = pb + i;
+      const float part = tile_partial<M, GU>(sl[i], xp, sx);
+      if (act && pass < p.NP) {
+        const int slot = pass * p.P + tid;
+        part_s[slot] = part;
+#pragma unroll
+        for (int gi = 0; gi < GU; gi++) meta_s[slot * GU + gi] = sl[i].meta[gi];
+      }
+      const int np = pass + D;
+      const int row = r0 + np * p.rpp + rip;
+      issue(sl[i], rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && np < p.NP && row < p.R);
+    }
+  }
+  __syncthreads();
+
+  // --- side-record corrections: (P - W_main) x_c, W_main = lo + s (q - 1/2 + 2^(1-M)).
+  constexpr float kHeld = -0.5f + 1.0f / float(1 << (M - 1));
+  const int chunk = kEntries * nthr;
+  auto correction = [&](uint32_t colq, uint32_t pbits, int rloc) -> float {
+    const int c = int(colq & 0x3fffffffu);
+    const int q = int(colq >> 30);
+    const int tile = c >> 7;
+    const int slot = (rloc / p.rpp) * p.P + (rloc % p.rpp) * p.T + tile;
+    const int gi = (c & 127) / p.g;
+    const uint32_t mw = meta_s[slot * GU + gi];
+    const float lo = h2f(mw & 0xffffu), st = h2f(mw >> 16);
+    const float wmain = lo + st * (float(q) + kHeld);
+    return (h2f(pbits) - wmain) * h2f(xs[c]);
+  };
+#pragma unroll
+  for (int j = 0; j < kEntries; j++) {
+    const int e = e0 + tid + j * nthr;
+    if (e < e1) corr_s[e - e0] = correction(cq[j], pv[j], erow[j]);
+  }
+  __syncthreads();
+  for (int i = tid; i < p.RB; i += nthr) {
+    const int a = max(rp[i], e0), b = min(rp[i + 1], e0 + chunk);
+    float acc = 0.f;
+    for (int e = a; e < b; e++) acc += corr_s[e - e0];
+    rowcorr_s[i] = acc;
+  }
+  // Rare: more entries than one prefetched chunk.
+  for (int ce = e0 + chunk; ce < e1; ce += chunk) {
+    __syncthreads();
+    for (int j = 0; j < kEntries; j++) {
+      const int e = ce + tid + j * nthr;
+      if (e < e1) {
+        int lo = 0, hi = p.RB;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (rp[mid] <= e) lo = mid; else hi = mid;
+        }
+        corr_s[e - ce] = correction(ld32(rCq, uint32_t(e) * 4u), ld16(rVal, uint32_t(e) * 2u), lo);
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < p.RB; i += nthr) {
+      const int a = max(rp[i], ce), b = min(rp[i + 1], ce + chunk);
+      float acc = rowcorr_s[i];
+      for (int e = a; e < b; e++) acc += corr_s[e - ce];
+      rowcorr_s[i] = acc;
+    }
+  }
+  __syncthreads();
+
+  // --- row sums: L lanes per row, fixed order, then a butterfly.
+  const int L = p.L;
+  const int lam = tid & (L - 1);
+  for (int i = tid / L; i < p.RB; i += nthr / L) {
+    const int base = (i / p.rpp) * p.P + (i % p.rpp) * p.T;
+    float acc = (lam == 0) ? rowcorr_s[i] : 0.f;
+    for (int tt = lam; tt < p.T; tt += L) acc += part_s[base + tt];
+    for (int off = L >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off, L);
+    if (lam == 0 && r0 + i < p.R) p.y[r0 + i] = acc;
+  }
+}
+
+// Code dump: one thread per tile writes the 128 codes u_M of its tile.
+struct CodesParams {
+  const uint8_t* s0;
+  const uint8_t* planes;
+  uint8_t* codes;
+  uint32_t chunk_bytes;
+  int32_t T, C;
+  int64_t tiles;
+};
+
+template <int M>
+__global__ void __launch_bounds__(256) codes_kernel(const CodesParams p) {
+  const int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (u >= p.tiles) return;
+  const rsrc_t rA = mk(p.s0, p.chunk_bytes), rB = mk(p.s0 + p.chunk_bytes, p.chunk_bytes);
+  const uint32_t off = uint32_t(u) * 16u;
+  const u32x4 a = ld128(rA, off), b = ld128(rB, off);
+  u32x4 pl[M > 2 ? M - 2 : 1];
+#pragma unroll
+  for (int k = 0; k < M - 2; k++) pl[k] = ld128(mk(p.planes + uint64_t(k) * p.chunk_bytes, p.chunk_bytes), off);
+  uint32_t out[32];  // out[8d + m] = codes of columns 32d + 4m .. 32d + 4m + 3
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    if constexpr (M == 2) {
+#pragma unroll
+      for (int m = 0; m < 8; m++) {
+        uint32_t o = 0;
+#pragma unroll
+        for (int bb = 0; bb < 4; bb++) {
+          const uint32_t w = s0_dword(a, b, 2 * d + (bb & 1));
+          o |= ((w >> (2 * (2 * m + (bb >> 1)))) & 3u) << (8 * bb);
+        }
+        out[8 * d + m] = o;
+      }
+    } else {
+      uint32_t ye, yo;
+      if constexpr (M >= 4) {
+        pair_fields(pl[0][d], pl[1][d], ye, yo);
+      } else {
+        ye = (pl[0][d] << 1) & 0xAAAAAAAAu;
+        yo = pl[0][d] & 0xAAAAAAAAu;
+      }
+      uint32_t ve = 0, vo = 0, we = 0, wo = 0;
+      if constexpr (M >= 5) {
+        if constexpr (M >= 6) pair_fields(pl[2][d], pl[3][d], ve, vo);
+        else { ve = (pl[2][d] << 1) & 0xAAAAAAAAu; vo = pl[2][d] & 0xAAAAAAAAu; }
+        if constexpr (M >= 7) {
+          if constexpr (M >= 8) pair_fields(pl[4][d], pl[5][d], we, wo);
+          else { we = (pl[4][d] << 1) & 0xAAAAAAAAu; wo = pl[4][d] & 0xAAAAAAAAu; }
+        }
+      }
+      uint32_t z[2][2], v[2][2];
+#pragma unroll
+      for (int e = 0; e < 2; e++) {
+        nibbles(s0_dword(a, b, 2 * d + e), e ? yo : ye, z[e][0], z[e][1]);
+        nibbles(e ? vo : ve, e ? wo : we, v[e][0], v[e][1]);
+      }
+#pragma unroll
+      for (int m = 0; m < 8; m++) {
+        uint32_t o = 0;
+#pragma unroll
+        for (int bb = 0; bb < 4; bb++) {
+          const int e = bb & 1, h = bb >> 1;
+          const uint32_t n0 = (z[e][h] >> (4 * m)) & 15u;   // q b3 b4 (zeros below a short read)
+          uint32_t code;
+          if constexpr (M == 3) code = n0 >> 1;
+          else if constexpr (M == 4) code = n0;
+          else code = (n0 << (M - 4)) | (((v[e][h] >> (4 * m)) & 15u) >> (8 - M));
+          o |= code << (8 * bb);
+        }
+        out[8 * d + m] = o;
+      }
+    }
+  }
+  const int64_t row = u / p.T, tc = u % p.T;
+  u32x4* dst = reinterpret_cast<u32x4*>(p.codes + row * p.C + tc * 128);
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    u32x4 v;
+    v[0] = out[4 * i]; v[1] = out[4 * i + 1]; v[2] = out[4 * i + 2]; v[3] = out[4 * i + 3];
+    dst[i] = v;
+  }
+}
+
+}  // namespace dev
+
+// ------------------------------------------------------------- dispatch ----
+struct LaunchCfg {
+  int waves, rpp, NP, RB, grid, L;
+  size_t lds;
+  dev::GemvParams prm;
+};
+
+static int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+static int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : dflt;
+}
+
+constexpr size_t kLdsBudget = 64 * 1024;
+constexpr int kMaxWaves = 8;  // matches __launch_bounds__(512) of the GEMV kernel
+
+// LDS carve-up of one workgroup: x, row_ptr slice, group pairs and partials of
+// every tile it owns, side-record corrections, per-row correction sums.
+static size_t lds_layout(int C, int GU, int nthr, int NP, int rpp, int P, dev::GemvParams* prm) {
+  const size_t units = size_t(NP) * P;
+  const int RB = NP * rpp;
+  size_t o = (size_t(C) * 2 + 15) & ~size_t(15);
+  if (prm) prm->lds_rp = uint32_t(o);
+  o += size_t(RB + 1) * 4;
+  o = (o + 15) & ~size_t(15);
+  if (prm) prm->lds_meta = uint32_t(o);
+  o += units * 4 * GU;
+  if (prm) prm->lds_part = uint32_t(o);
+  o += units * 4;
+  if (prm) prm->lds_corr = uint32_t(o);
+  o += size_t(dev::kEntries) * nthr * 4;
+  if (prm) prm->lds_rowcorr = uint32_t(o);
+  o += size_t(RB) * 4;
+  return o;
+}
+
+// Launch shape for one GEMV: k waves per workgroup, rpp rows side by side
+// (rpp * tiles_per_row lanes busy), NP passes, so that every CU gets about the
+// same number of rows.  STAGQ_WAVES / STAGQ_NP override the choice (tuning).
+static bool plan_gemv(const ImageHeader& h, int GU, LaunchCfg* c) {
+  const int T = h.cols / kTileCols;
+  const int R = h.rows;
+  const int cus = device_cus();
+  const int kmin = std::max(std::max((T + 63) / 64, 1),
+                            (h.cols / 8 + dev::kXChunks * 64 - 1) / (dev::kXChunks * 64));
+  auto util = [&](int k) { return double((64 * k / T) * T) / (64.0 * k); };
+  auto grid1 = [&](int k) {  // workgroups at one pass each
+    const int rpp = 64 * k / T;
+    return rpp > 0 ? (R + rpp - 1) / rpp : 0;
+  };
+  int best = 0;
+  const int order[8] = {4, 5, 6, 7, 8, 3, 2, 1};
+  for (int k : order)  // first well-filled shape, preferring about 4 waves
+    if (k >= kmin && util(k) >= 0.97) { best = k; break; }
+  if (!best) {
+    double bu = -1.0;
+    for (int k = kmin; k <= kMaxWaves; k++)
+      if (util(k) > bu + 1e-9) { bu = util(k); best = k; }
+  }
+  if (best > 1 && grid1(best) < cus)  // small matrices: smaller groups to reach every CU
+    for (int k = best - 1; k >= kmin; k--)
+      if (util(k) >= 0.97) { best = k; if (grid1(k) >= cus) break; }
+  const int k = env_int("STAGQ_WAVES", best);
+  if (k < kmin || k > kMaxWaves) return false;
+  const int nthr = 64 * k;
+  const int rpp = nthr / T;
+  if (rpp < 1) return false;
+  const int passes = (R + rpp - 1) / rpp;
+  const int P = rpp * T;
+  auto fits = [&](int np) {
+    return lds_layout(h.cols, GU, nthr, np, rpp, P, nullptr) <= kLdsBudget &&
+           np * rpp + 1 <= 2 * nthr;
+  };
+  // Passes per workgroup: the fewest rounds of workgroups per CU, each round
+  // costing its passes plus about two passes of prologue.
+  int NP = 0;
+  double best_cost = 1e300;
+  for (int np = 1; np <= passes; np++) {
+    if (!fits(np)) break;
+    const int grid = (passes + np - 1) / np;
+    const double cost = double((grid + cus - 1) / cus) * (np + 2.0);
+    if (cost < best_cost - 1e-9) { best_cost = cost; NP = np; }
+    if (grid <= cus) break;
+  }
+  NP = env_int("STAGQ_NP", NP);
+  if (NP < 1 || !fits(NP)) return false;
+  const int RB = NP * rpp;
+  c->waves = k; c->rpp = rpp; c->NP = NP; c->RB = RB;
+  c->grid = (R + RB - 1) / RB;
+  int L = 1;
+  while (L < 16 && 2 * L * RB <= nthr) L *= 2;
+  c->L = L;
+  c->lds = lds_layout(h.cols, GU, nthr, NP, rpp, P, &c->prm);
+  c->prm.R = R; c->prm.C = h.cols; c->prm.T = T; c->prm.g = h.group; c->prm.rpp = rpp;
+  c->prm.P = P; c->prm.NP = NP; c->prm.RB = RB; c->prm.L = L;
+  return true;
+}
+
+template <int M, int GU, int D>
+static hipError_t launch_gemv(const LaunchCfg& c, hipStream_t st) {
+  hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D>), dim3(c.grid), dim3(64 * c.waves), c.lds, st, c.prm);
+  return hipGetLastError();
+}
+
+template <int M, int GU>
+static hipError_t launch_gemv_d(const LaunchCfg& c, hipStream_t st) {
+  return launch_gemv<M, GU, (M == 2 ? 4 : 2)>(c, st);
+}
+
+template <int M>
+static hipError_t launch_gemv_m(int GU, const LaunchCfg& c, hipStream_t st) {
+  switch (GU) {
+    case 1: return launch_gemv_d<M, 1>(c, st);
+    case 2: return launch_gemv_d<M, 2>(c, st);
+    default: return launch_gemv_d<M, 4>(c, st);
+  }
+}
+
+template <int M>
+static hipError_t launch_codes(const dev::CodesParams& p, hipStream_t st) {
+  const unsigned blocks = unsigned((p.tiles + 255) / 256);
+  hipLaunchKernelGGL((dev::codes_kernel<M>), dim3(blocks), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace stagq
+
+using namespace stagq;
+
+extern "C" {
+
+static int make_handle(const ImageHeader& h, const void* dev, stagq_handle* out) {
+  stagq_handle hd = new (std::nothrow) stagq_handle_s;
+  if (!hd) return STAGQ_EINVAL;
+  hd->hdr = h;
+  hd->dev = static_cast<const uint8_t*>(dev);
+  *out = hd;
+  return STAGQ_OK;
+}
+
+int stagq_pack(const stagq_fields* f, void* dev_buf, size_t dev_bytes, void* hip_stream,
+               stagq_handle* out) {
+  if (!out || !dev_buf) return STAGQ_EINVAL;
+  ImageHeader h;
+  int st = validate_fields(f, &h);
+  if (st != STAGQ_OK) return st;
+  if (reinterpret_cast<uintptr_t>(dev_buf) % 256) return STAGQ_EALIGN;
+  if (dev_bytes < h.total) return STAGQ_ESIZE;
+  void* host = nullptr;
+  if (hipHostMalloc(&host, size_t(h.total), hipHostMallocDefault) != hipSuccess) return STAGQ_EHIP;
+  st = stagq_pack_host(f, host, size_t(h.total));
+  if (st == STAGQ_OK) {
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (hipMemcpyAsync(dev_buf, host, size_t(h.total), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      st = STAGQ_EHIP;
+  }
+  hipHostFree(host);
+  if (st != STAGQ_OK) return st;
+  return make_handle(h, dev_buf, out);
+}
+
+int stagq_rebind(stagq_handle h, void* dev_buf, size_t dev_bytes, stagq_handle* out) {
+  if (!h || !dev_buf || !out) return STAGQ_EINVAL;
+  if (reinterpret_cast<uintptr_t>(dev_buf) % 256) return STAGQ_EALIGN;
+  if (dev_bytes < h->hdr.total) return STAGQ_ESIZE;
+  return make_handle(h->hdr, dev_buf, out);
+}
+
+int stagq_query(stagq_handle h, stagq_info* out) {
+  if (!h || !out) return STAGQ_EINVAL;
+  memset(out, 0, sizeof(*out));
+  out->rows = h->hdr.rows; out->cols = h->hdr.cols; out->group = h->hdr.group;
+  out->nbits_max = h->hdr.nbits; out->nnz = h->hdr.nnz; out->image_bytes = h->hdr.total;
+  for (int b = 2; b <= h->hdr.nbits; b++) out->bytes_read[b] = bytes_read(h->hdr, b);
+  return STAGQ_OK;
+}
+
+void stagq_destroy(stagq_handle h) { delete h; }
+
+int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stream) {
+  if (!h) return STAGQ_EINVAL;
+  const ImageHeader& H = h->hdr;
+  if (bits < 2 || bits > H.nbits) return STAGQ_EBITS;
+  if (H.rows == 0) return STAGQ_OK;  // nothing to compute; y may be empty
+  if (!x || !y) return STAGQ_EINVAL;
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 4) return STAGQ_EALIGN;
+  const int GU = kTileCols / H.group;
+  LaunchCfg c;
+  if (!plan_gemv(H, GU, &c)) return STAGQ_ESHAPE;
+  const uint8_t* b = h->dev;
+  c.prm.s0 = b + H.off_s0;
+  c.prm.planes = b + H.off_planes;
+  c.prm.meta = b + H.off_meta;
+  c.prm.row_ptr = b + H.off_rowptr;
+  c.prm.colq = b + H.off_colq;
+  c.prm.val = b + H.off_val;
+  c.prm.x = static_cast<const uint8_t*>(x);
+  c.prm.y = y;
+  c.prm.chunk_bytes = uint32_t(H.bytes_s0_chunk);
+  c.prm.meta_bytes = uint32_t(H.bytes_meta);
+  c.prm.colq_bytes = uint32_t(H.nnz * 4);
+  c.prm.val_bytes = uint32_t(H.nnz * 2);
+  c.prm.rp_bytes = uint32_t((H.rows + 1) * 4);
+  c.prm.x_bytes = uint32_t(H.cols * 2);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t err;
+  switch (bits) {
+    case 2: err = launch_gemv_m<2>(GU, c, st); break;
+    case 3: err = launch_gemv_m<3>(GU, c, st); break;
+    case 4: err = launch_gemv_m<4>(GU, c, st); break;
+    case 5: err = launch_gemv_m<5>(GU, c, st); break;
+    case 6: err = launch_gemv_m<6>(GU, c, st); break;
+    case 7: err = launch_gemv_m<7>(GU, c, st); break;
+    default: err = launch_gemv_m<8>(GU, c, st); break;
+  }
+  return err == hipSuccess ? STAGQ_OK : STAGQ_EHIP;
+}
+
+int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int bits,
+                    int32_t* out) {
+  if (!out) return STAGQ_EINVAL;
+  ImageHeader H;
+  if (!layout(rows, cols, group, nbits, 0, &H)) return STAGQ_ESHAPE;
+  if (bits < 2 || bits > nbits) return STAGQ_EBITS;
+  LaunchCfg c;
+  if (!plan_gemv(H, kTileCols / group, &c)) return STAGQ_ESHAPE;
+  out[0] = c.grid; out[1] = 64 * c.waves; out[2] = c.rpp; out[3] = c.NP; out[4] = c.RB;
+  out[5] = int32_t(c.lds); out[6] = c.L; out[7] = (bits == 2) ? 4 : 2;
+  return STAGQ_OK;
+}
+
+int stagq_decode_codes(stagq_handle h, int bits, uint8_t* codes, void* hip_stream) {
+  if (!h) return STAGQ_EINVAL;
+  const ImageHeader& H = h->hdr;
+  if (bits < 2 || bits > H.nbits) return STAGQ_EBITS;
+  if (H.tiles == 0) return STAGQ_OK;
+  if (!codes) return STAGQ_EINVAL;
+  if (reinterpret_cast<uintptr_t>(codes) % 16) return STAGQ_EALIGN;
+  dev::CodesParams p;
+  p.s0 = h->dev + H.off_s0;
+  p.planes = h->dev + H.off_planes;
+  p.codes = codes;
+  p.chunk_bytes = uint32_t(H.bytes_s0_chunk);
+  p.T = H.cols / kTileCols;
+  p.C = H.cols;
+  p.tiles = H.tiles;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t err;
+  switch (bits) {
+    case 2: err = launch_codes<2>(p, st); break;
+    case 3: err = launch_codes<3>(p, st); break;
+    case 4: err = launch_codes<4>(p, st); break;
+    case 5: err = launch_codes<5>(p, st); break;
+    case 6: err = launch_codes<6>(p, st); break;
+    case 7: err = launch_codes<7>(p, st); break;
+    default: err = launch_codes<8>(p, st); break;
+  }
+  return err == hipSuccess ? STAGQ_OK : STAGQ_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,396 @@
+// Host half of the StagQ library: validation, the plane-major packer, its
+// inverse, the traffic model and the reference-grade encoder.  No HIP calls.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
+#include <thread>
+#include <utility>
+#include <vector>
+
+#include "stagq_internal.h"
+
+namespace stagq {
+
+// ---------------------------------------------------------------- fp16 ----
+double half_to_double(uint16_t h) {
+  const int sgn = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 0) v = ldexp(double(m), -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp(double(m | 1024), e - 25);
+  return sgn ? -v : v;
+}
+
+// Round-to-nearest-even conversion written out on the binary64 bit pattern.
+uint16_t double_to_half(double v) {
+  uint64_t b;
+  memcpy(&b, &v, 8);
+  const uint16_t sgn = uint16_t((b >> 48) & 0x8000u);
+  const int e = int((b >> 52) & 0x7ff);
+  const uint64_t frac = b & ((uint64_t(1) << 52) - 1);
+  if (e == 0x7ff) return uint16_t(sgn | 0x7c00u | (frac ? 0x200u : 0u));
+  if (e == 0) return sgn;                       // binary64 subnormals are far below half's range
+  const int E = e - 1023;                       // value = 1.frac * 2^E
+  if (E > 15) return uint16_t(sgn | 0x7c00u);   // overflow
+  const uint64_t mant = frac | (uint64_t(1) << 52);
+  const int shift = (E >= -14) ? 42 : 28 - E;   // bits dropped to reach half's ulp
+  if (shift >= 64) return sgn;
+  uint64_t qv = mant >> shift;
+  const uint64_t rem = mant & ((uint64_t(1) << shift) - 1);
+  const uint64_t halfway = uint64_t(1) << (shift - 1);
+  if (rem > halfway || (rem == halfway && (qv & 1))) qv++;
+  uint32_t bits = (E >= -14) ? (uint32_t(E + 15) << 10) + uint32_t(qv - 1024) : uint32_t(qv);
+  if (bits >= 0x7c00u) bits = 0x7c00u;          // rounded up into infinity
+  return uint16_t(sgn | bits);
+}
+
+static bool half_finite(uint16_t h) { return ((h >> 10) & 31) != 31; }
+
+// ------------------------------------------------------------- validate ----
+int validate_fields(const stagq_fields* f, ImageHeader* h) {
+  if (!f) return STAGQ_EINVAL;
+  if (!layout(f->rows, f->cols, f->group, f->nbits_max, f->nnz, h)) return STAGQ_ESHAPE;
+  const int64_t R = f->rows, C = f->cols, G = C / f->group, N = f->nbits_max;
+  if (R > 0 && (!f->q || !f->lo || !f->s || (N > 2 && !f->planes))) return STAGQ_EINVAL;
+  if (!f->row_ptr) return STAGQ_EINVAL;
+  if (f->nnz > 0 && (!f->col || !f->val)) return STAGQ_EINVAL;
+  const int64_t n = R * C;
+  for (int64_t i = 0; i < n; i++)
+    if (f->q[i] > 3) return STAGQ_EFIELD;
+  for (int64_t i = 0; i < (N - 2) * n; i++)
+    if (f->planes[i] > 1) return STAGQ_EFIELD;
+  for (int64_t i = 0; i < R * G; i++)
+    if (!half_finite(f->lo[i]) || !half_finite(f->s[i])) return STAGQ_EFIELD;
+  if (f->row_ptr[0] != 0 || f->row_ptr[R] != f->nnz) return STAGQ_ECSR;
+  for (int64_t r = 0; r < R; r++) {
+    const int64_t a = f->row_ptr[r], b = f->row_ptr[r + 1];
+    if (b < a || a < 0 || b > f->nnz) return STAGQ_ECSR;
+    for (int64_t e = a; e < b; e++) {
+      const int64_t c = f->col[e];
+      if (c < 0 || c >= C) return STAGQ_ECSR;
+      if (e > a && c <= f->col[e - 1]) return STAGQ_ECSR;
+      if (!half_finite(f->val[e])) return STAGQ_EFIELD;
+      for (int64_t k = 0; k < N - 2; k++)
+        if (f->planes[k * n + r * C + c]) return STAGQ_EFIELD;  // planes skip held-out entries
+    }
+  }
+  return STAGQ_OK;
+}
+
+uint64_t bytes_read(const ImageHeader& h, int bits) {
+  const uint64_t n = uint64_t(h.rows) * h.cols;
+  return n * 2 / 8 + n * uint64_t(bits - 2) / 8 + h.bytes_meta + uint64_t(h.rows + 1) * 4 +
+         uint64_t(h.nnz) * 6 + uint64_t(h.cols) * 2 + uint64_t(h.rows) * 4;
+}
+
+// ----------------------------------------------------------------- pack ----
+static void pack_tiles(const stagq_fields* f, const ImageHeader& h, uint8_t* img, int64_t u0,
+                       int64_t u1) {
+  const int64_t C = f->cols, n = int64_t(f->rows) * C, T = C / kTileCols;
+  const int N = f->nbits_max;
+  uint32_t* s0a = reinterpret_cast<uint32_t*>(img + h.off_s0);
+  uint32_t* s0b = reinterpret_cast<uint32_t*>(img + h.off_s0 + h.bytes_s0_chunk);
+  for (int64_t u = u0; u < u1; u++) {
+    const int64_t r = u / T, c0 = (u % T) * kTileCols;
+    const uint8_t* q = f->q + r * C + c0;
+    for (int d = 0; d < 4; d++)
+      for (int e = 0; e < 2; e++) {
+        uint32_t w = 0;
+        for (int j = 0; j < 16; j++) w |= uint32_t(q[32 * d + 2 * j + e]) << (2 * j);
+        const int dw = 2 * d + e;
+        (dw < 4 ? s0a : s0b)[u * 4 + (dw & 3)] = w;
+      }
+    for (int k = 3; k <= N; k++) {
+      uint32_t* pl = reinterpret_cast<uint32_t*>(img + h.off_planes + uint64_t(k - 3) * h.bytes_plane);
+      const uint8_t* b = f->planes + int64_t(k - 3) * n + r * C + c0;
+      for (int d = 0; d < 4; d++) {
+        uint32_t w = 0;
+        for (int t = 0; t < 32; t++) w |= uint32_t(b[32 * d + t]) << t;
+        pl[u * 4 + d] = w;
+      }
+    }
+  }
+}
+
+template <class F>
+static void parallel_for(int64_t n, F fn) {
+  unsigned nt = std::thread::hardware_concurrency();
+  if (const char* e = getenv("STAGQ_HOST_THREADS")) nt = unsigned(atoi(e));
+  if (nt < 1) nt = 1;
+  if (nt > 64) nt = 64;
+  if (n < 4096 || nt == 1) { fn(int64_t(0), n); return; }
+  std::vector<std::thread> th;
+  const int64_t step = (n + nt - 1) / nt;
+  for (unsigned i = 0; i < nt; i++) {
+    const int64_t a = int64_t(i) * step, b = std::min(n, a + step);
+    if (a < b) th.emplace_back(fn, a, b);
+  }
+  for (auto& t : th) t.join();
+}
+
+}  // namespace stagq
+
+using namespace stagq;
+
+extern "C" {
+
+const char* stagq_strerror(int status) {
+  switch (status) {
+    case STAGQ_OK: return "ok";
+    case STAGQ_EINVAL: return "invalid argument";
+    case STAGQ_EBITS: return "bits outside [2, N]";
+    case STAGQ_ESHAPE: return "unsupported shape (cols % 128, group in {32,64,128}, 2 <= N <= 8, streams < 2 GiB)";
+    case STAGQ_ECSR: return "malformed side record";
+    case STAGQ_EALIGN: return "misaligned pointer";
+    case STAGQ_EHIP: return "HIP runtime error";
+    case STAGQ_EFIELD: return "field value out of range";
+    case STAGQ_ESIZE: return "buffer too small";
+    case STAGQ_EIMAGE: return "not a packed StagQ image";
+    default: return "unknown status";
+  }
+}
+
+size_t stagq_packed_bytes(const stagq_fields* f) {
+  if (!f) return 0;
+  ImageHeader h;
+  if (!layout(f->rows, f->cols, f->group, f->nbits_max, f->nnz, &h)) return 0;
+  return size_t(h.total);
+}
+
+int stagq_pack_host(const stagq_fields* f, void* dst, size_t dst_bytes) {
+  ImageHeader h;
+  const int st = validate_fields(f, &h);
+  if (st != STAGQ_OK) return st;
+  if (!dst) return STAGQ_EINVAL;
+  if (reinterpret_cast<uintptr_t>(dst) % 16) return STAGQ_EALIGN;
+  if (dst_bytes < h.total) return STAGQ_ESIZE;
+  uint8_t* img = static_cast<uint8_t*>(dst);
+  memset(img, 0, size_t(h.total));
+  memcpy(img, &h, sizeof(h));
+  parallel_for(h.tiles, [&](int64_t a, int64_t b) { pack_tiles(f, h, img, a, b); });
+  const int64_t R = f->rows, G = f->cols / f->group;
+  uint32_t* meta = reinterpret_cast<uint32_t*>(img + h.off_meta);
+  for (int64_t i = 0; i < R * G; i++) meta[i] = uint32_t(f->lo[i]) | (uint32_t(f->s[i]) << 16);
+  memcpy(img + h.off_rowptr, f->row_ptr, size_t(R + 1) * 4);
+  uint32_t* colq = reinterpret_cast<uint32_t*>(img + h.off_colq);
+  uint16_t* val = reinterpret_cast<uint16_t*>(img + h.off_val);
+  for (int64_t r = 0; r < R; r++)
+    for (int64_t e = f->row_ptr[r]; e < f->row_ptr[r + 1]; e++) {
+      const uint32_t c = uint32_t(f->col[e]);
+      colq[e] = c | (uint32_t(f->q[r * f->cols + c]) << 30);
+      val[e] = f->val[e];
+    }
+  return STAGQ_OK;
+}
+
+int stagq_unpack_host(const void* image, size_t image_bytes, stagq_info* shape, uint8_t* q,
+                      uint8_t* planes, uint16_t* lo, uint16_t* s, int32_t* row_ptr, int32_t* col,
+                      uint16_t* val) {
+  if (!image || !shape) return STAGQ_EINVAL;
+  if (image_bytes < sizeof(ImageHeader)) return STAGQ_ESIZE;
+  ImageHeader h;
+  memcpy(&h, image, sizeof(h));
+  if (h.magic != kImageMagic || h.version != kImageVersion) return STAGQ_EIMAGE;
+  ImageHeader chk;
+  if (!layout(h.rows, h.cols, h.group, h.nbits, h.nnz, &chk) || chk.total != h.total)
+    return STAGQ_EIMAGE;
+  if (image_bytes < h.total) return STAGQ_ESIZE;
+  memset(shape, 0, sizeof(*shape));
+  shape->rows = h.rows; shape->cols = h.cols; shape->group = h.group; shape->nbits_max = h.nbits;
+  shape->nnz = h.nnz; shape->image_bytes = h.total;
+  for (int b = 2; b <= h.nbits; b++) shape->bytes_read[b] = bytes_read(h, b);
+  const uint8_t* img = static_cast<const uint8_t*>(image);
+  const int64_t C = h.cols, T = C / kTileCols, n = int64_t(h.rows) * C;
+  if (q) {
+    const uint32_t* s0a = reinterpret_cast<const uint32_t*>(img + h.off_s0);
+    const uint32_t* s0b = reinterpret_cast<const uint32_t*>(img + h.off_s0 + h.bytes_s0_chunk);
+    for (int64_t u = 0; u < h.tiles; u++)
+      for (int dw = 0; dw < 8; dw++) {
+        const uint32_t w = (dw < 4 ? s0a : s0b)[u * 4 + (dw & 3)];
+        const int d = dw >> 1, e = dw & 1;
+        for (int j = 0; j < 16; j++)
+          q[(u / T) * C + (u % T) * kTileCols + 32 * d + 2 * j + e] = uint8_t((w >> (2 * j)) & 3);
+      }
+  }
+  if (planes)
+    for (int k = 3; k <= h.nbits; k++) {
+      const uint32_t* pl =
+          reinterpret_cast<const uint32_t*>(img + h.off_planes + uint64_t(k - 3) * h.bytes_plane);
+      for (int64_t u = 0; u < h.tiles; u++)
+        for (int d = 0; d < 4; d++)
+          for (int t = 0; t < 32; t++)
+            planes[int64_t(k - 3) * n + (u / T) * C + (u % T) * kTileCols + 32 * d + t] =
+                uint8_t((pl[u * 4 + d] >> t) & 1);
+    }
+  const uint32_t* meta = reinterpret_cast<const uint32_t*>(img + h.off_meta);
+  const int64_t ng = int64_t(h.rows) * (C / h.group);
+  for (int64_t i = 0; i < ng; i++) {
+    if (lo) lo[i] = uint16_t(meta[i] & 0xffff);
+    if (s) s[i] = uint16_t(meta[i] >> 16);
+  }
+  if (row_ptr) memcpy(row_ptr, img + h.off_rowptr, size_t(h.rows + 1) * 4);
+  const uint32_t* colq = reinterpret_cast<const uint32_t*>(img + h.off_colq);
+  const uint16_t* v = reinterpret_cast<const uint16_t*>(img + h.off_val);
+  for (int64_t e = 0; e < h.nnz; e++) {
+    if (col) col[e] = int32_t(colq[e] & 0x3fffffffu);
+    if (val) val[e] = v[e];
+  }
+  return STAGQ_OK;
+}
+
+// -------------------------------------------------------------- encoder ----
+// Written from the encoder description of the StagQ paper (section 3.5-3.6,
+// Appendix E) with the same readings as the project's documentation: ratio
+// pre-grid guard ranked by the ratio (ties by flat index), min-max pair over
+// the kept entries stored as fp16, nearest base code with ties upward,
+// post-grid guard on the largest |w - (lo + s q)| over the matrix (ties by flat
+// index), sign planes skipping held-out entries and zero-step groups.
+int stagq_encode(const uint16_t* w16, int32_t rows, int32_t cols, int32_t group, int32_t nbits,
+                 int64_t budget, double ratio_T, uint8_t* q, uint8_t* planes, uint16_t* lo16,
+                 uint16_t* s16, int32_t* row_ptr, int32_t* col, uint16_t* val, int64_t* n_pre_out) {
+  if (rows < 0 || cols <= 0 || group <= 0 || cols % group || nbits < 2 || nbits > kMaxBits)
+    return STAGQ_ESHAPE;
+  const int64_t R = rows, C = cols, g = group, G = C / g, n = R * C;
+  if (budget < 0 || budget > n || budget >= (int64_t(1) << 31)) return STAGQ_EINVAL;
+  if (n > 0 && (!w16 || !q || !lo16 || !s16 || (nbits > 2 && !planes))) return STAGQ_EINVAL;
+  if (!row_ptr || (budget > 0 && (!col || !val))) return STAGQ_EINVAL;
+
+  std::vector<uint8_t> held(size_t(n), 0);
+  // 1. pre-grid guard: one candidate per group at most.
+  struct Cand { double ratio; int64_t flat; };
+  std::vector<Cand> cand_all;
+  {
+    std::vector<std::vector<Cand>> part(64);
+    std::atomic<int> slot{0};
+    parallel_for(R * G, [&](int64_t a, int64_t b) {
+      std::vector<Cand>& out = part[size_t(slot.fetch_add(1))];
+      for (int64_t grp = a; grp < b; grp++) {
+        const int64_t base = (grp / G) * C + (grp % G) * g;
+        int64_t imax = 0;
+        double amax = -1.0;
+        for (int64_t i = 0; i < g; i++) {
+          const double m = fabs(half_to_double(w16[base + i]));
+          if (m > amax) { amax = m; imax = i; }
+        }
+        double second = -1.0;
+        for (int64_t i = 0; i < g; i++)
+          if (i != imax) second = std::max(second, fabs(half_to_double(w16[base + i])));
+        if (amax > ratio_T * second)
+          out.push_back(Cand{second > 0.0 ? amax / second : INFINITY, base + imax});
+      }
+    });
+    for (auto& p : part) cand_all.insert(cand_all.end(), p.begin(), p.end());
+  }
+  auto by_ratio = [](const Cand& x, const Cand& y) {
+    return x.ratio > y.ratio || (x.ratio == y.ratio && x.flat < y.flat);
+  };
+  std::sort(cand_all.begin(), cand_all.end(), by_ratio);
+  const int64_t n_pre = std::min<int64_t>(budget, int64_t(cand_all.size()));
+  for (int64_t i = 0; i < n_pre; i++) held[size_t(cand_all[size_t(i)].flat)] = 1;
+
+  // 2-3. pair fit over kept entries, nearest base code for every entry.
+  parallel_for(R * G, [&](int64_t a, int64_t b) {
+    for (int64_t grp = a; grp < b; grp++) {
+      const int64_t base = (grp / G) * C + (grp % G) * g;
+      double mn = INFINITY, mx = -INFINITY;
+      for (int64_t i = 0; i < g; i++)
+        if (!held[size_t(base + i)]) {
+          const double v = half_to_double(w16[base + i]);
+          mn = std::min(mn, v); mx = std::max(mx, v);
+        }
+      const uint16_t l16 = double_to_half(mn), st16 = double_to_half((mx - mn) / 3.0);
+      lo16[grp] = l16; s16[grp] = st16;
+      const double L = half_to_double(l16), S = half_to_double(st16);
+      for (int64_t i = 0; i < g; i++) {
+        const double d = half_to_double(w16[base + i]) - L;
+        int qq = 0;
+        if (S > 0.0)
+          for (int j = 0; j < 3; j++) qq += (d >= (j + 0.5) * S) ? 1 : 0;
+        q[base + i] = uint8_t(qq);
+      }
+    }
+  });
+
+  // 4. post-grid guard: the budget left, on the largest two-bit residuals.
+  const int64_t n_post = budget - n_pre;
+  if (n_post > 0) {
+    struct Res { double r; int64_t flat; };
+    auto by_res = [](const Res& x, const Res& y) {
+      return x.r > y.r || (x.r == y.r && x.flat < y.flat);
+    };
+    const int64_t nblk = std::max<int64_t>(1, std::min<int64_t>(64, (n + (1 << 20) - 1) >> 20));
+    std::vector<std::vector<Res>> best(static_cast<size_t>(nblk));
+    std::atomic<int64_t> next{0};
+    auto worker = [&]() {
+      for (int64_t bk; (bk = next.fetch_add(1)) < nblk;) {
+        const int64_t a = n * bk / nblk, b = n * (bk + 1) / nblk;
+        std::vector<Res> v;
+        v.reserve(size_t(b - a));
+        for (int64_t i = a; i < b; i++) {
+          if (held[size_t(i)]) continue;
+          const int64_t grp = (i / C) * G + (i % C) / g;
+          const double rec = half_to_double(lo16[grp]) + half_to_double(s16[grp]) * q[i];
+          v.push_back(Res{fabs(half_to_double(w16[i]) - rec), i});
+        }
+        if (int64_t(v.size()) > n_post) {
+          std::nth_element(v.begin(), v.begin() + n_post, v.end(), by_res);
+          v.resize(size_t(n_post));
+        }
+        best[size_t(bk)] = std::move(v);
+      }
+    };
+    unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    std::vector<std::thread> th;
+    for (unsigned i = 0; i < nt; i++) th.emplace_back(worker);
+    for (auto& t : th) t.join();
+    std::vector<Res> all;
+    for (auto& v : best) all.insert(all.end(), v.begin(), v.end());
+    if (int64_t(all.size()) > n_post) {
+      std::nth_element(all.begin(), all.begin() + n_post, all.end(), by_res);
+      all.resize(size_t(n_post));
+    }
+    for (const Res& x : all) held[size_t(x.flat)] = 1;
+  }
+
+  // 5. planes: sign of the residual of the preceding prefix, sign(0) = +1.
+  parallel_for(R * G, [&](int64_t a, int64_t b) {
+    for (int64_t grp = a; grp < b; grp++) {
+      const int64_t base = (grp / G) * C + (grp % G) * g;
+      const double L = half_to_double(lo16[grp]), S = half_to_double(s16[grp]);
+      for (int64_t i = 0; i < g; i++) {
+        const int64_t idx = base + i;
+        const double wv = half_to_double(w16[idx]);
+        double rec = L + S * q[idx];
+        const bool active = !held[size_t(idx)] && S > 0.0;
+        for (int k = 3; k <= nbits; k++) {
+          uint8_t bit = 0;
+          if (active) {
+            bit = (wv - rec >= 0.0) ? 1 : 0;
+            rec += (2.0 * bit - 1.0) * S / double(int64_t(1) << (k - 1));
+          }
+          planes[int64_t(k - 3) * n + idx] = bit;
+        }
+      }
+    }
+  });
+
+  // 6. side record as CSR in (row, col) order.
+  int64_t e = 0;
+  row_ptr[0] = 0;
+  for (int64_t r = 0; r < R; r++) {
+    for (int64_t c = 0; c < C; c++)
+      if (held[size_t(r * C + c)]) {
+        col[e] = int32_t(c);
+        val[e] = w16[r * C + c];
+        e++;
+      }
+    row_ptr[r + 1] = int32_t(e);
+  }
+  if (n_pre_out) *n_pre_out = n_pre;
+  return e == budget ? STAGQ_OK : STAGQ_EINVAL;
+}
+
+}  // extern "C"

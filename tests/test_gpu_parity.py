@@ -1,0 +1,247 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Decoded codes must match the oracle bit for bit; y must be within relative L2
+error 1e-3 of the oracle's float64 GEMV (the StagQ GEMV target).  A stricter
+regression bound is checked too, scaled the way floating-point dot products
+err: ||y - y_ref|| <= 1e-5 * || |W_hat| |x| || (fp32 accumulation over a few
+thousand terms stays near 1e-7 of that scale).  Every case prints its name
+before touching the GPU.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import WORKLOADS, synth_matrix
+
+pytestmark = pytest.mark.gpu
+
+REL_L2_CONTRACT = 1e-3
+REL_L2_REGRESSION = 1e-5
+
+
+def _say(*a):
+    print("[gpu]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def pwo():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import precision_weight_only_amd as m   # raises if libstagq.so is missing
+    return m
+
+
+def _to_dev(x16):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x16).view(np.int16)).view(torch.float16).cuda()
+
+
+def _rel(y, ref):
+    return float(np.linalg.norm(y.astype(np.float64) - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def _abs_scale(F, x, M, rows=None):
+    """|| |W_hat| |x| ||_2, the natural scale of the rounding error of y."""
+    ax = np.abs(np.asarray(x, np.float64))
+    out = np.empty(F.rows)
+    for r0 in range(0, F.rows, 8192):
+        r1 = min(F.rows, r0 + 8192)
+        out[r0:r1] = np.abs(oracle.w_hat(F, M, slice(r0, r1))) @ ax
+    return float(np.linalg.norm(out))
+
+
+def _regression_ok(y, ref, F, x, M):
+    return float(np.linalg.norm(y.astype(np.float64) - ref)) <= REL_L2_REGRESSION * _abs_scale(F, x, M)
+
+
+@functools.lru_cache(maxsize=4)
+def _encoded(workload, mname):
+    wl = WORKLOADS[workload]
+    mat = [m for m in wl.matrices if m.name == mname][0]
+    w, x = synth_matrix(mat.rows, mat.cols, wl.dist, mat.seed)
+    F = oracle.encode(w, wl.group, wl.nbits, wl.frac, wl.ratio_T)
+    return F, x
+
+
+def _check(pwo, F, x, bits, tag, codes_rows=None):
+    m = pwo.StagQMatrix.pack(F)
+    xd = _to_dev(x)
+    for M in bits:
+        _say(tag, f"bits={M}", f"shape={F.rows}x{F.cols}", f"g={F.group}", f"nnz={F.nnz}")
+        got = m.decode_codes(M)
+        want = oracle.codes(F, M)
+        if codes_rows is None:
+            assert np.array_equal(got.cpu().numpy(), want), f"codes differ at bits={M}"
+        else:
+            assert np.array_equal(got[codes_rows].cpu().numpy(), want[codes_rows])
+        del got
+        y = m.gemv(xd, M).cpu().numpy()
+        ref = oracle.gemv(F, x, M)
+        rel = _rel(y, ref)
+        _say(tag, f"bits={M} rel_l2={rel:.3e}")
+        assert rel <= REL_L2_CONTRACT
+        assert _regression_ok(y, ref, F, x, M)
+    return m, xd
+
+
+FULL = [(wl, m.name) for wl in ("tiny", "attn", "mlp", "phi4_mlp") for m in WORKLOADS[wl].matrices]
+SWEEP = [m.name for m in WORKLOADS["layer_sweep"].matrices if m.name != "lm_head"]
+
+
+@pytest.mark.parametrize("workload,mname", FULL, ids=[f"{a}-{b}" for a, b in FULL])
+def test_workload_parity(pwo, workload, mname):
+    F, x = _encoded(workload, mname)
+    _check(pwo, F, x, WORKLOADS[workload].bits, f"{workload}/{mname}")
+
+
+@pytest.mark.parametrize("mname", SWEEP)
+def test_layer_sweep_bits_switched_per_call(pwo, mname):
+    """One packed stream, the precision switched on every call (2, 3, 4, 2, ...)."""
+    import torch
+    wl = WORKLOADS["layer_sweep"]
+    F, x = _encoded("layer_sweep", mname)
+    m = pwo.StagQMatrix.pack(F)
+    xd = _to_dev(x)
+    refs = {M: oracle.gemv(F, x, M) for M in wl.bits}
+    ys = []
+    for i in range(9):
+        M = wl.bits[i % 3]
+        _say(f"layer_sweep/{mname}", f"call {i} bits={M}")
+        ys.append((M, m.gemv(xd, M)))
+    torch.cuda.synchronize()
+    for M, y in ys:
+        assert _rel(y.cpu().numpy(), refs[M]) <= REL_L2_CONTRACT
+        assert _regression_ok(y.cpu().numpy(), refs[M], F, x, M)
+    for M in wl.bits:  # same bits -> bitwise identical results
+        same = [y.cpu().numpy() for b, y in ys if b == M]
+        assert all(np.array_equal(same[0], s) for s in same[1:])
+
+
+def _tile_rows(F, reps, rows):
+    """Fields of a taller matrix whose row r repeats row r % F.rows."""
+    idx = np.arange(rows) % F.rows
+    counts = np.diff(F.row_ptr)[idx]
+    row_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    starts = F.row_ptr[idx]
+    sel = np.concatenate([np.arange(a, a + c) for a, c in zip(starts, counts)]) if counts.sum() else np.zeros(0, int)
+    return oracle.Fields(rows, F.cols, F.group, F.nbits, F.q[idx], F.planes[:, idx], F.lo[idx], F.s[idx],
+                         F.mask[idx], row_ptr, F.col[sel], F.val[sel])
+
+
+def test_lm_head_full_size(pwo):
+    """128256 x 4096 LM head at its real shape and launch configuration.  The
+    fields repeat the oracle encoding of a 4096 x 4096 Student-t matrix (seed 7)
+    row-wise, so the expected y is the oracle's y of that matrix repeated."""
+    wl = WORKLOADS["layer_sweep"]
+    w, x = synth_matrix(4096, 4096, wl.dist, 7)
+    Fs = oracle.encode(w, wl.group, wl.nbits, wl.frac, wl.ratio_T)
+    F = _tile_rows(Fs, 32, 128256)
+    m = pwo.StagQMatrix.pack(F)
+    xd = _to_dev(x)
+    rows = np.arange(128256)
+    sample = np.unique(np.concatenate([rows[:64], rows[-64:], np.random.default_rng(0).choice(128256, 512)]))
+    for M in wl.bits:
+        _say("lm_head", f"bits={M}")
+        got = m.decode_codes(M)[sample].cpu().numpy()
+        assert np.array_equal(got, oracle.codes(Fs, M)[sample % 4096])
+        y = m.gemv(xd, M).cpu().numpy()
+        ref = np.tile(oracle.gemv(Fs, x, M), 32)[:128256]
+        assert _rel(y, ref) <= REL_L2_CONTRACT
+        assert float(np.linalg.norm(y - ref)) <= REL_L2_REGRESSION * _abs_scale(Fs, x, M) * np.sqrt(128256 / 4096)
+
+
+# ------------------------------------------------------------- edge cases
+EDGE = [
+    # (rows, cols, group, nbits, frac, dist, seed)
+    (1, 128, 128, 4, 0.0, "student_t", 1),        # one row, one tile, no side record
+    (1001, 384, 64, 4, 0.01, "student_t", 2),     # ragged rows, 3 tiles per row
+    (77, 640, 32, 6, 0.02, "normal_outliers", 3),  # g = 32, 5 tiles, N = 6
+    (300, 1024, 128, 8, 0.005, "student_t", 4),    # N = 8: every precision 2..8
+    (64, 4096, 128, 4, 0.1, "student_t", 5),       # more entries than one prefetched chunk
+    (513, 8320, 64, 5, 0.001, "student_t", 6),     # 65 tiles per row (> one wave)
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"{c[0]}x{c[1]}g{c[2]}N{c[3]}" for c in EDGE])
+def test_edge_shapes(pwo, case):
+    R, Cc, g, N, frac, dist, seed = case
+    w, x = synth_matrix(R, Cc, dist, seed)
+    F = oracle.encode(w, g, N, frac)
+    _check(pwo, F, x, range(2, N + 1), f"edge{case}")
+
+
+def test_degenerate_values(pwo):
+    """Constant groups (stored step 0), zero x, fp16 subnormal x, a held-out entry
+    in every group."""
+    rng = np.random.default_rng(12)
+    w = (0.02 * rng.standard_normal((96, 512))).astype(np.float16)
+    w[:8] = np.float16(0.5)                     # constant rows -> s = 0
+    w[8:16, ::64] = np.float16(3.0)             # an extreme entry in every group
+    F = oracle.encode(w, 64, 4, 0.02)
+    assert np.all(F.s[:8] == 0)
+    for x in (np.zeros(512, np.float16),
+              (rng.standard_normal(512) * 1e-6).astype(np.float16),   # mostly subnormal
+              rng.standard_normal(512).astype(np.float16)):
+        m = pwo.StagQMatrix.pack(F)
+        xd = _to_dev(x)
+        for M in (2, 3, 4):
+            y = m.gemv(xd, M).cpu().numpy()
+            ref = oracle.gemv(F, x, M)
+            if not np.any(ref):
+                assert not np.any(y)
+            else:
+                assert _rel(y, ref) <= REL_L2_CONTRACT
+                assert _regression_ok(y, ref, F, x, M)
+
+
+def test_empty_matrix(pwo):
+    import torch
+    F = oracle.encode(np.zeros((0, 256), np.float16), 128, 4, 0.0)
+    m = pwo.StagQMatrix.pack(F)
+    y = m.gemv(_to_dev(np.ones(256, np.float16)), 3)
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+
+
+def test_deterministic(pwo):
+    import torch
+    F, x = _encoded("tiny", "W")
+    m = pwo.StagQMatrix.pack(F)
+    xd = _to_dev(x)
+    for M in (2, 3, 4):
+        a = m.gemv(xd, M).clone()
+        b = m.gemv(xd, M).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_copies_decode_identically(pwo):
+    """A rebound copy of the image (as used for cache-cold timing) gives the same y."""
+    import torch
+    F, x = _encoded("tiny", "W")
+    m = pwo.StagQMatrix.pack(F)
+    c = m.replicate()
+    xd = _to_dev(x)
+    for M in (2, 3, 4):
+        assert torch.equal(m.gemv(xd, M), c.gemv(xd, M))
+
+
+def test_error_codes(pwo):
+    import torch
+    F, x = _encoded("tiny", "W")
+    m = pwo.StagQMatrix.pack(F)
+    xd = _to_dev(x)
+    for bad in (1, 5, 0, -3):
+        with pytest.raises(pwo.StagQError) as e:
+            m.gemv(xd, bad)
+        assert e.value.status == -2
+    xbig = torch.zeros(F.cols + 8, dtype=torch.float16, device="cuda")
+    with pytest.raises(pwo.StagQError) as e:
+        m.gemv(xbig[1:], 3)                      # 2-byte offset: not 16-byte aligned
+    assert e.value.status == -5
+    with pytest.raises(pwo.StagQError) as e:
+        m.decode_codes(7)
+    assert e.value.status == -2

@@ -1,0 +1,150 @@
+"""Host-side checks of the native library (no GPU): exported symbols, the
+plane-major packer and its inverse, argument validation, the fp16 rounding of
+the encoder, and the library encoder against the oracle encoder (bit-exact)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import precision_weight_only_amd as pwo
+from precision_weight_only_amd import _lib
+from workloads import WORKLOADS, synth_matrix
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_header_symbols_are_exported():
+    with open(os.path.join(ROOT, "include", "stagq.h")) as f:
+        text = f.read()
+    code = re.sub(r"/\*.*?\*/", "", text, flags=re.S)          # drop comments
+    declared = set(re.findall(r"\b(stagq_[a-z_]+)\s*\(", code))
+    assert declared == set(_lib.EXPORTED)
+    lib = pwo.lib()
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+@pytest.mark.parametrize("shape", [(256, 512, 64, 4, 0.005), (33, 384, 32, 6, 0.02), (5, 1024, 128, 8, 0.01)])
+def test_library_encoder_matches_oracle(shape):
+    R, Cc, g, N, frac = shape
+    w, _ = synth_matrix(R, Cc, "normal_outliers", 17)
+    F = oracle.encode(w, g, N, frac)
+    E = pwo.encode(w, g, N, F.nnz)
+    for k in ("q", "planes", "row_ptr", "col"):
+        assert np.array_equal(getattr(F, k), E[k]), k
+    for k in ("lo", "s", "val"):
+        assert np.array_equal(getattr(F, k).view(np.uint16), E[k].view(np.uint16)), k
+    assert E["n_pre"] == F.n_pre
+
+
+def test_library_encoder_matches_oracle_student_t_full_row_width():
+    wl = WORKLOADS["attn"]
+    w, _ = synth_matrix(512, 4096, wl.dist, 3)
+    F = oracle.encode(w, wl.group, wl.nbits, wl.frac)
+    E = pwo.encode(w, wl.group, wl.nbits, F.nnz)
+    assert all(np.array_equal(getattr(F, k), E[k]) for k in ("q", "planes", "row_ptr", "col"))
+
+
+def test_fp16_rounding_of_the_step_matches_numpy():
+    """The library's float64 -> fp16 conversion (round to nearest even) on values
+    built around fp16 rounding boundaries, via one-row groups whose step is the
+    value under test: s16 = fp16((max - min) / 3)."""
+    rng = np.random.default_rng(5)
+    base = rng.uniform(-3, 3, 4000).astype(np.float16).astype(np.float64)
+    w = np.zeros((4000, 32), np.float16)
+    w[:, 0] = 0
+    w[:, 1] = base.astype(np.float16)
+    w[:, 2:] = (base[:, None] / 2).astype(np.float16)
+    F = oracle.encode(w, 32, 2, 0.0)
+    E = pwo.encode(w, 32, 2, 0)
+    assert np.array_equal(F.s.view(np.uint16), E["s"].view(np.uint16))
+
+
+def test_pack_roundtrip_and_size():
+    w, _ = synth_matrix(64, 640, "normal_outliers", 2)
+    F = oracle.encode(w, 64, 6, 0.01)
+    img = pwo.pack_host(F)
+    assert img.size == pwo.packed_bytes(F)
+    U = pwo.unpack_host(img)
+    for k in ("q", "planes", "row_ptr", "col"):
+        assert np.array_equal(getattr(F, k), U[k]), k
+    for k in ("lo", "s", "val"):
+        assert np.array_equal(getattr(F, k).view(np.uint16), U[k].view(np.uint16)), k
+
+
+def test_plane_major_layout_offsets():
+    """A read at precision M touches the base stream and planes 3..M only: the
+    planes follow the base stream in order of k, each R*C/8 bytes."""
+    w, _ = synth_matrix(16, 256, "student_t", 4)
+    F = oracle.encode(w, 128, 6, 0.0)
+    img = pwo.pack_host(F)
+    hdr = np.frombuffer(img[:256].tobytes(), dtype=np.uint64)
+    off_s0, off_planes = int(hdr[5]), int(hdr[6])
+    n = 16 * 256
+    assert off_planes - off_s0 >= n // 4
+    # Flipping one refinement bit in the fields changes exactly one plane's bytes.
+    F2 = oracle.Fields(**{**F.__dict__})
+    F2.planes = F.planes.copy()
+    F2.planes[2, 3, 77] ^= 1
+    img2 = pwo.pack_host(F2)
+    diff = np.nonzero(img != img2)[0]
+    assert diff.size == 1
+    assert off_planes + 2 * (n // 8) <= diff[0] < off_planes + 3 * (n // 8)
+
+
+def test_bytes_read_model():
+    F = oracle.encode(synth_matrix(32, 1024, "student_t", 1)[0], 128, 4, 0.001)
+    img = pwo.pack_host(F)
+    U = pwo.unpack_host(img)
+    info = _lib.Info()
+    pwo.lib().stagq_unpack_host(img.ctypes.data_as(C.c_void_p), img.size, C.byref(info),
+                                None, None, None, None, None, None, None)
+    n = 32 * 1024
+    for M in (2, 3, 4):
+        want = n * M // 8 + 32 * 8 * 4 + 33 * 4 + F.nnz * 6 + 1024 * 2 + 32 * 4
+        assert info.bytes_read[M] == want
+    assert U["nnz"] == F.nnz
+
+
+def _bad(F, **over):
+    d = dict(F.__dict__)
+    d.update(over)
+    return oracle.Fields(**d)
+
+
+def test_validation_errors():
+    w, _ = synth_matrix(8, 256, "normal_outliers", 9)
+    F = oracle.encode(w, 64, 4, 0.01)
+    assert F.nnz > 0
+    q = F.q.copy(); q[0, 0] = 4
+    cases = {
+        -7: [_bad(F, q=q)],
+        -4: [_bad(F, row_ptr=np.concatenate([[1], F.row_ptr[1:]]).astype(np.int32)),
+             _bad(F, col=np.where(np.arange(F.nnz) == 0, 999, F.col).astype(np.int32))],
+    }
+    planes = F.planes.copy()
+    r = int(np.searchsorted(F.row_ptr, 0, side="right") - 1)
+    planes[0, r, F.col[0]] = 1                       # a plane bit at a held-out position
+    cases[-7].append(_bad(F, planes=planes))
+    for status, fs in cases.items():
+        for f in fs:
+            with pytest.raises(pwo.StagQError) as e:
+                pwo.pack_host(f)
+            assert e.value.status == status
+    with pytest.raises(pwo.StagQError) as e:
+        pwo.pack_host(_bad(F, cols=200, q=F.q[:, :200]))
+    assert e.value.status in (-3, -7, -4)
+
+
+def test_unsupported_shapes():
+    for (R, Cc, g, N) in [(4, 100, 50, 4), (4, 256, 16, 4), (4, 256, 128, 9), (4, 256, 128, 1)]:
+        assert pwo.lib().stagq_plan_gemv(R, Cc, g, N, 2, (C.c_int32 * 8)()) == -3
+    assert pwo.lib().stagq_plan_gemv(4, 256, 128, 4, 5, (C.c_int32 * 8)()) == -2
+
+
+def test_strerror_covers_every_status():
+    for st in range(0, -10, -1):
+        assert pwo.lib().stagq_strerror(st).decode() != "unknown status"
