@@ -1,0 +1,242 @@
+"""Benchmark of the StagQ batch-one GEMV on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode graph|eager]
+
+Workload: the Llama-3.1-8B gate/up projection, W 14336 x 4096 (rows = output
+channels), Student-t (nu = 4) weights scaled to std 0.02, group 128, base +
+2 planes (2/3/4-bit prefixes), side record 0.1 % of the weights, x ~ N(0, 1)
+fp16, batch one.  Weights are synthetic (seeded) and encoded by the library's
+host encoder; nothing is read from disk.
+
+One step = one GEMV at each precision 2, 3 and 4 bits, each on a different copy
+of the packed image: copies rotate so that consecutive launches never touch
+the same bytes and the working set (>= 700 MB) exceeds the 256 MB Infinity
+Cache, so every launch streams its weights from HBM.  The K timed steps run as
+three captured HIP graphs, one per precision with K launches each (--mode
+graph, default); timing events recorded between the replays on the stream the
+kernels run on give the mean duration of each precision's launches.  --mode
+eager launches from Python with an event pair around every launch instead.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD public specification
+METRIC = "µs per batch-1 GEMV and effective HBM GB/s (% of peak) at 2/3/4 bits"
+A100_STAGQ_US = {2: 23.7, 3: 28.9, 4: 32.8}   # the paper's Table 8, 8B gate/up, A100 40 GB, g = 32
+KERNEL_SRC = os.path.join(ROOT, "precision_weight_only_amd", "csrc", "stagq_device.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_14336x4096_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch measured by rocprofv3 counters (FETCH_SIZE, WRITE_SIZE),
+    valid only while the kernel source is the one they were taken on."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    out = {}
+    for b, val in re.findall(r"traffic_bytes_per_launch\[(\d)\]:\s*([0-9.eE+]+)", text):
+        out[int(b)] = float(val)
+    return out or None
+
+
+def cpu_baseline(rows_sample: int = 1024, target_s: float = 12.0):
+    """The oracle's float64 decode + matvec on the host, on a row sample of the
+    same workload (oracle-encoded), repeated for about target_s seconds."""
+    import oracle
+    from workloads import WORKLOADS, synth_matrix
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = 1
+    wl = WORKLOADS["mlp"]
+    w, x = synth_matrix(rows_sample, 4096, wl.dist, 0)
+    F = oracle.encode(w, wl.group, wl.nbits, wl.frac, wl.ratio_T)
+    G = 4096 // wl.group
+    nbytes = {M: rows_sample * 4096 * M // 8 + rows_sample * G * 4 + F.nnz * 6 + (rows_sample + 1) * 4
+              + 4096 * 2 + rows_sample * 4 for M in wl.bits}
+    t0 = time.perf_counter()
+    done = 0
+    moved = 0
+    while time.perf_counter() - t0 < target_s or done < 3:
+        for M in wl.bits:
+            oracle.gemv(F, x, M)
+            moved += nbytes[M]
+        done += 1
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+        "sample": f"{rows_sample}x4096 rows of the same Student-t workload (oracle-encoded), "
+                  f"float64 decode (Eq. 9) + side record + matvec at bits 2,3,4, {done} rounds in {dt:.1f} s; "
+                  f"elementwise NumPy on 1 thread, BLAS matvec on {blas} threads; "
+                  f"host has {os.cpu_count()} logical CPUs",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
+    ap.add_argument("--rot-mb", type=int, default=768, help="total size of the rotated image copies")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 (the GEMV path has "
+              "no multi-GPU leg).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import precision_weight_only_amd as pwo
+    from workloads import WORKLOADS, synth_matrix
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS["mlp"]
+    mat = wl.matrices[0]                       # gate/up 14336 x 4096
+    R, Cc = mat.rows, mat.cols
+    bits = list(wl.bits)
+
+    t0 = time.time()
+    w, x = synth_matrix(R, Cc, wl.dist, mat.seed)
+    K = int(np.floor(wl.frac * R * Cc + 0.5))
+    fields = pwo.encode(w, wl.group, wl.nbits, K, wl.ratio_T)
+    base = pwo.StagQMatrix.pack(fields, device=dev)
+    n_copies = max(6, -(-args.rot_mb * (1 << 20) // base.image_bytes))
+    n_copies += (-n_copies) % 3
+    copies = [base] + [base.replicate() for _ in range(n_copies - 1)]
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.float16).to(dev)
+    ys = [torch.empty(R, dtype=torch.float32, device=dev) for _ in range(n_copies)]
+    setup_s = time.time() - t0
+    stream = torch.cuda.current_stream()
+
+    def launch(i, M):
+        c = i % n_copies
+        copies[c].gemv(xd, M, y=ys[c])
+
+    # warmup (also loads the code objects)
+    for s in range(args.warmup):
+        for j, M in enumerate(bits):
+            launch(3 * s + j, M)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    order = {M: [3 * s + j for s in range(K)] for j, M in enumerate(bits)}   # launch ids per precision
+    dur = {M: [] for M in bits}
+
+    if args.mode == "graph":
+        # One graph per precision holding K launches on rotating copies; timing
+        # events sit between the replays on the same stream (ROCm does not allow
+        # timing events inside a captured graph).
+        graphs = {}
+        for M in bits:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in order[M]:
+                    launch(i, M)
+            graphs[M] = g
+            g.replay()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(bits) + 1)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        evs[0].record()
+        for j, M in enumerate(bits):
+            graphs[M].replay()
+            evs[j + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        for j, M in enumerate(bits):
+            dur[M] = [evs[j].elapsed_time(evs[j + 1]) * 1e3 / K] * K     # microseconds per launch
+    else:
+        # Eager launches with a timing event pair around every launch.
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(3 * K)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for s in range(K):
+            for j, M in enumerate(bits):
+                i = 3 * s + j
+                ev[i][0].record()
+                launch(i, M)
+                ev[i][1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        for j, M in enumerate(bits):
+            dur[M] = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in order[M]]
+
+    bytes_alg = {M: base.bytes_read[M] for M in bits}
+    per_bits = {}
+    for M in bits:
+        d = np.array(dur[M])
+        mean = float(d.mean())
+        per_bits[str(M)] = {
+            "us_mean": round(mean, 3), "us_median": round(float(np.median(d)), 3),
+            "us_p10": round(float(np.percentile(d, 10)), 3), "us_p90": round(float(np.percentile(d, 90)), 3),
+            "bytes": int(bytes_alg[M]),
+            "gbps": round(bytes_alg[M] / (mean * 1e-6) / 1e9, 1),
+            "pct_peak": round(100.0 * bytes_alg[M] / (mean * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+            "a100_stagq_us": A100_STAGQ_US[M],
+            "launch": pwo.plan_gemv(R, Cc, wl.group, wl.nbits, M),
+        }
+    step_bytes = sum(bytes_alg.values())
+    value = step_bytes * K / wall / 1e9
+
+    traffic = read_traffic()
+    dom = 4                                        # the 4-bit read moves the most bytes per step
+    ach = per_bits[str(dom)]["gbps"]
+    roofline = {
+        "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": round(ach / PEAK_HBM_GBS, 4),
+        "traffic": (traffic or {}).get(dom),
+        "kernel": f"gemv_kernel<M={dom}> (bits={dom})",
+        "by_bits": {str(M): {"achieved": per_bits[str(M)]["gbps"],
+                             "frac": round(per_bits[str(M)]["gbps"] / PEAK_HBM_GBS, 4),
+                             "traffic": (traffic or {}).get(M)} for M in bits},
+    }
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B gate/up GEMV 14336x4096, Student-t(4) std 0.02, g=128, "
+                               "base + 2 planes, side record 0.1%, batch 1",
+                   "rows": R, "cols": Cc, "group": wl.group, "nbits": wl.nbits, "bits": bits,
+                   "side_record_nnz": int(base.nnz), "image_bytes": int(base.image_bytes),
+                   "rotation_copies": n_copies, "mode": args.mode,
+                   "step": "one GEMV at each of 2, 3, 4 bits, each on its own image copy"},
+        "per_bits": per_bits,
+        "roofline": roofline,
+        "setup_s": round(setup_s, 2),
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -176,6 +176,9 @@ class StagQMatrix:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h and _lib_mod._lib is not None:
-            _lib_mod._lib.stagq_destroy(h)
-            self._h = None
+        try:
+            if h and _lib_mod._lib is not None:
+                _lib_mod._lib.stagq_destroy(h)
+        except Exception:       # interpreter shutdown: modules already torn down
+            pass
+        self._h = None

@@ -99,8 +99,8 @@ struct GemvParams {
   const uint8_t* x;
   float* y;
   uint32_t chunk_bytes, meta_bytes, colq_bytes, val_bytes, rp_bytes, x_bytes;
-  int32_t R, C, T, g, rpp, P, NP, RB, L;
-  uint32_t lds_rp, lds_meta, lds_part, lds_corr, lds_rowcorr;
+  int32_t R, C, T, g, rpp, P, NP, RB, L, rb_pow2;
+  uint32_t lds_rp, lds_meta, lds_part, lds_corr, lds_rowcorr, lds_dummy;
 };
 
 template <int M, int GU>
@@ -240,6 +240,38 @@ __device__ __forceinline__ float tile_partial(const Slot<M, GU>& s, const uint32
   return part;
 }
 
+// Sum over aligned groups of N lanes (N = 8 or 16) with a DPP row_shr
+// inclusive scan; lane N-1 of each group ends up with the group's total.
+// Fixed order, so the result is reproducible.
+template <int SH>
+__device__ __forceinline__ float add_row_shr(float v) {
+  const int xv = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + SH, 0xf, 0xf, true);
+  return v + __builtin_bit_cast(float, xv);
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16, "DPP row_shr works inside 16-lane rows");
+  v = add_row_shr<1>(v);
+  v = add_row_shr<2>(v);
+  v = add_row_shr<4>(v);
+  if constexpr (N == 16) v = add_row_shr<8>(v);
+  return v;
+}
+constexpr int kLG = 16;  // lanes per row group in the final reductions
+
+// One step of a segmented inclusive scan inside 16-lane rows (DPP row_shr):
+// add the value SH lanes down when it belongs to the same row id r.
+template <int SH>
+__device__ __forceinline__ float seg_step(float v, int r) {
+  const int pv = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + SH, 0xf, 0xf, true);
+  const int pr = __builtin_amdgcn_update_dpp(-1, r, 0x110 + SH, 0xf, 0xf, false);
+  return pr == r ? v + __builtin_bit_cast(float, pv) : v;
+}
+
+// LDS column index of x: every 128-column tile is followed by 16 bytes of
+// padding, so lanes reading their own tiles hit different banks.
+__device__ __forceinline__ int xcol(int c) { return c + ((c >> 7) << 3); }
+
 template <int M, int GU, int D>
 __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
@@ -267,7 +299,13 @@ __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
   const rsrc_t rCq = mk(p.colq, p.colq_bytes);
   const rsrc_t rVal = mk(p.val, p.val_bytes);
 
-  // --- prologue: x and row_ptr first, then the first D passes of weights.
+  // --- prologue: row_ptr and x first (needed first), then D passes of weights.
+  uint32_t rpv[2];  // row_ptr[r0 .. r0 + RB], clamped at R (RB + 1 <= 2 * nthr)
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int j = tid + i * nthr;
+    rpv[i] = ld32(rRp, j <= p.RB ? uint32_t(min(r0 + j, p.R)) * 4u : kOOB);
+  }
   const int xchunks = p.C >> 3;
   u32x4 xv[kXChunks];
 #pragma unroll
@@ -275,57 +313,45 @@ __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
     const int ci = tid + i * nthr;
     xv[i] = ld128(rX, ci < xchunks ? uint32_t(ci) * 16u : kOOB);
   }
-  uint32_t rpv[2];  // row_ptr[r0 .. r0 + RB], clamped at R (RB + 1 <= 2 * nthr)
+  __builtin_amdgcn_sched_barrier(0);     // row_ptr and x stay ahead of the weight loads
+  // Only the first pass is requested before x: x and row_ptr queue behind
+  // whatever is in flight, so the rest of the weights follow the barrier.
+  Slot<M, GU> sl[D];
+  {
+    const int row = r0 + rip;
+    issue(sl[0], rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && 0 < p.NP && row < p.R);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // The LDS writes below are unconditional (out-of-range slots go to a per-thread
+  // scratch area): a load whose value is only used under a branch would be sunk
+  // into it and waited on after the weight loads, delaying the barrier until
+  // the first D passes of weights had arrived.
+  uint8_t* dummy = lds + p.lds_dummy + tid * 16;
 #pragma unroll
   for (int i = 0; i < 2; i++) {
     const int j = tid + i * nthr;
-    rpv[i] = ld32(rRp, j <= p.RB ? uint32_t(min(r0 + j, p.R)) * 4u : kOOB);
+    *reinterpret_cast<int32_t*>(j <= p.RB ? reinterpret_cast<uint8_t*>(rp + j) : dummy) = int32_t(rpv[i]);
   }
-
-  Slot<M, GU> sl[D];
-#pragma unroll
-  for (int i = 0; i < D; i++) {
-    const int row = r0 + i * p.rpp + rip;
-    issue(sl[i], rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && i < p.NP && row < p.R);
-  }
-
 #pragma unroll
   for (int i = 0; i < kXChunks; i++) {
     const int ci = tid + i * nthr;
-    if (ci < xchunks) *reinterpret_cast<u32x4*>(xs + ci * 8) = xv[i];
+    *reinterpret_cast<u32x4*>(ci < xchunks ? reinterpret_cast<uint8_t*>(xs + xcol(ci * 8)) : dummy) = xv[i];
   }
-#pragma unroll
-  for (int i = 0; i < 2; i++)
-    if (tid + i * nthr <= p.RB) rp[tid + i * nthr] = int32_t(rpv[i]);
-  for (int i = tid; i < p.RB; i += nthr) rowcorr_s[i] = 0.f;
   __syncthreads();
-
-  // --- side record: prefetch this workgroup's first entries, find their rows.
-  const int e0 = rp[0], e1 = rp[p.RB];
-  uint32_t cq[kEntries], pv[kEntries];
-  int erow[kEntries];
 #pragma unroll
-  for (int j = 0; j < kEntries; j++) {
-    const int e = e0 + tid + j * nthr;
-    const bool ok = e < e1;
-    cq[j] = ld32(rCq, ok ? uint32_t(e) * 4u : kOOB);
-    pv[j] = ld16(rVal, ok ? uint32_t(e) * 2u : kOOB);
-    int lo = 0, hi = p.RB;           // rp[lo] <= e < rp[hi]
-    if (ok) {
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (rp[mid] <= e) lo = mid; else hi = mid;
-      }
-    }
-    erow[j] = lo;
+  for (int i = 1; i < D; i++) {          // slot by slot: pass i's loads complete first
+    const int row = r0 + i * p.rpp + rip;
+    issue(sl[i], rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && i < p.NP && row < p.R);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  const int e0 = rp[0], e1 = rp[p.RB];
 
   // --- x slice of this lane's tile as permuted fp16 pairs; per-group sum(x).
   uint32_t xp[64];
   float sx[GU];
 #pragma unroll
   for (int gi = 0; gi < GU; gi++) sx[gi] = 0.f;
-  const uint16_t* xt = xs + (act ? t : 0) * 128;
+  const uint16_t* xt = xs + xcol((act ? t : 0) * 128);
 #pragma unroll
   for (int d = 0; d < 4; d++) {
     uint32_t xr[64];
@@ -356,84 +382,152 @@ __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
     }
   }
 
-  // --- main loop over passes, D passes of loads in flight.
-  for (int pb = 0; pb < p.NP; pb += D) {
-#pragma unroll
-    for (int i = 0; i < D; i++) {
-      const int pass = pb + i;
-      const float part = tile_partial<M, GU>(sl[i], xp, sx);
-      if (act && pass < p.NP) {
+  // --- main loop over passes, D passes of loads in flight.  After the first
+  //     pass, while later passes stream in, the workgroup's first side-record
+  //     entries are fetched and their rows found (branch-free binary search,
+  //     all entries in lockstep).
+  uint32_t cq[kEntries], pv[kEntries];
+  int erow[kEntries];
+  // One pass: its tile partial and group pairs go to LDS, then its slot is
+  // reloaded with pass + D (out of range -> zeros, no memory traffic), so the
+  // number of loads every wait counts is the same on every path.
+  auto step_pass = [&](Slot<M, GU>& sl_i, int pass) {
+    if (pass < p.NP) {
+      const float part = tile_partial<M, GU>(sl_i, xp, sx);
+      if (act) {
         const int slot = pass * p.P + tid;
         part_s[slot] = part;
 #pragma unroll
-        for (int gi = 0; gi < GU; gi++) meta_s[slot * GU + gi] = sl[i].meta[gi];
+        for (int gi = 0; gi < GU; gi++) meta_s[slot * GU + gi] = sl_i.meta[gi];
       }
-      const int np = pass + D;
-      const int row = r0 + np * p.rpp + rip;
-      issue(sl[i], rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && np < p.NP && row < p.R);
     }
+    const int np = pass + D;
+    const int row = r0 + np * p.rpp + rip;
+    issue(sl_i, rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && np < p.NP && row < p.R);
+  };
+  // The first D passes in straight-line code; after the first of them, while
+  // the others stream in, fetch this workgroup's first side-record entries and
+  // find their rows (branch-free binary search, all entries in lockstep).
+#pragma unroll
+  for (int i = 0; i < D; i++) {
+    step_pass(sl[i], i);
+    if (i == 0) {
+#pragma unroll
+      for (int j = 0; j < kEntries; j++) {
+        const int e = e0 + tid + j * nthr;
+        const bool ok = e < e1;
+        cq[j] = ld32(rCq, ok ? uint32_t(e) * 4u : kOOB);
+        pv[j] = ld16(rVal, ok ? uint32_t(e) * 2u : kOOB);
+        erow[j] = 0;
+      }
+      // rp[RB] = e1 > e, so clamping the probe at RB keeps the reads unconditional.
+      for (int step = p.rb_pow2; step > 0; step >>= 1) {
+        int probe[kEntries];
+#pragma unroll
+        for (int j = 0; j < kEntries; j++) probe[j] = rp[min(erow[j] + step, p.RB)];
+#pragma unroll
+        for (int j = 0; j < kEntries; j++)
+          if (probe[j] <= e0 + tid + j * nthr) erow[j] += step;
+      }
+    }
+  }
+  // Remaining passes (workgroups with more passes than loads in flight).
+  for (int pb = D; pb < p.NP; pb += D) {
+#pragma unroll
+    for (int i = 0; i < D; i++) step_pass(sl[i], pb + i);
   }
   __syncthreads();
 
-  // --- side-record corrections: (P - W_main) x_c, W_main = lo + s (q - 1/2 + 2^(1-M)).
+  // --- side-record corrections (P - W_main) x_c, W_main = lo + s (q - 1/2 + 2^(1-M)).
+  //     Entries are processed in chunks of kEntries * nthr in entry order; within
+  //     each block of 64 consecutive entries (one wave) a segmented inclusive scan
+  //     by row leaves, at the last entry of every row run, that run's sum.  Each
+  //     row then adds one value per 64-entry block it touches.  Fixed order.
   constexpr float kHeld = -0.5f + 1.0f / float(1 << (M - 1));
   const int chunk = kEntries * nthr;
+  const int lane = tid & 63;
   auto correction = [&](uint32_t colq, uint32_t pbits, int rloc) -> float {
     const int c = int(colq & 0x3fffffffu);
     const int q = int(colq >> 30);
-    const int tile = c >> 7;
-    const int slot = (rloc / p.rpp) * p.P + (rloc % p.rpp) * p.T + tile;
+    const int slot = (rloc / p.rpp) * p.P + (rloc % p.rpp) * p.T + (c >> 7);
     const int gi = (c & 127) / p.g;
     const uint32_t mw = meta_s[slot * GU + gi];
     const float lo = h2f(mw & 0xffffu), st = h2f(mw >> 16);
     const float wmain = lo + st * (float(q) + kHeld);
-    return (h2f(pbits) - wmain) * h2f(xs[c]);
+    return (h2f(pbits) - wmain) * h2f(xs[xcol(c)]);
   };
+  // Segmented inclusive scan over the 64 lanes: inside each 16-lane row with DPP
+  // shifts 1, 2, 4, 8, then carries from the last lane of the row before
+  // (covering 16 more lanes) and of the row two before (32 more), each added
+  // only when it belongs to the same row id (row ids are sorted by lane).
+  auto seg_scan = [&](float v, int r) -> float {
+    v = seg_step<1>(v, r);
+    v = seg_step<2>(v, r);
+    v = seg_step<4>(v, r);
+    v = seg_step<8>(v, r);
+    const int rs = lane & ~15;
+    {
+      const int src = rs > 0 ? rs - 1 : lane;
+      const float pv = __shfl(v, src, 64);
+      const int pr = __shfl(r, src, 64);
+      if (rs > 0 && pr == r) v += pv;
+    }
+    {
+      const int src = rs > 16 ? rs - 17 : lane;
+      const float pv = __shfl(v, src, 64);
+      const int pr = __shfl(r, src, 64);
+      if (rs > 16 && pr == r) v += pv;
+    }
+    return v;
+  };
+  float rowc[2] = {0.f, 0.f};             // this thread's rows: tid and tid + nthr
+  for (int ce = e0; ce < e1; ce += chunk) {
+    float sv[kEntries];
+    if (ce == e0) {
 #pragma unroll
-  for (int j = 0; j < kEntries; j++) {
-    const int e = e0 + tid + j * nthr;
-    if (e < e1) corr_s[e - e0] = correction(cq[j], pv[j], erow[j]);
-  }
-  __syncthreads();
-  for (int i = tid; i < p.RB; i += nthr) {
-    const int a = max(rp[i], e0), b = min(rp[i + 1], e0 + chunk);
-    float acc = 0.f;
-    for (int e = a; e < b; e++) acc += corr_s[e - e0];
-    rowcorr_s[i] = acc;
-  }
-  // Rare: more entries than one prefetched chunk.
-  for (int ce = e0 + chunk; ce < e1; ce += chunk) {
-    __syncthreads();
-    for (int j = 0; j < kEntries; j++) {
-      const int e = ce + tid + j * nthr;
-      if (e < e1) {
-        int lo = 0, hi = p.RB;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (rp[mid] <= e) lo = mid; else hi = mid;
-        }
-        corr_s[e - ce] = correction(ld32(rCq, uint32_t(e) * 4u), ld16(rVal, uint32_t(e) * 2u), lo);
+      for (int j = 0; j < kEntries; j++) {
+        const bool ok = e0 + tid + j * nthr < e1;
+        sv[j] = seg_scan(correction(cq[j], pv[j], erow[j]), ok ? erow[j] : p.RB);
+      }
+    } else {                              // rare: more entries than one prefetched chunk
+      __syncthreads();                    // previous chunk consumed
+#pragma unroll
+      for (int j = 0; j < kEntries; j++) {
+        const int e = ce + tid + j * nthr;
+        const bool ok = e < e1;
+        int lo = 0;
+        for (int step = p.rb_pow2; step > 0; step >>= 1)
+          if (rp[min(lo + step, p.RB)] <= e) lo += step;
+        const float cv = correction(ld32(rCq, ok ? uint32_t(e) * 4u : kOOB),
+                                    ld16(rVal, ok ? uint32_t(e) * 2u : kOOB), lo);
+        sv[j] = seg_scan(cv, ok ? lo : p.RB);
       }
     }
+#pragma unroll
+    for (int j = 0; j < kEntries; j++) corr_s[tid + j * nthr] = sv[j];
     __syncthreads();
-    for (int i = tid; i < p.RB; i += nthr) {
-      const int a = max(rp[i], ce), b = min(rp[i + 1], ce + chunk);
-      float acc = rowcorr_s[i];
-      for (int e = a; e < b; e++) acc += corr_s[e - ce];
-      rowcorr_s[i] = acc;
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      const int i = tid + k * nthr;
+      if (i < p.RB) {
+        const int a = max(rp[i], ce) - ce, b = min(rp[i + 1], ce + chunk) - ce;
+        for (int q = a; q < b; q = (q | 63) + 1) rowc[k] += corr_s[min(b, (q | 63) + 1) - 1];
+      }
     }
   }
-  __syncthreads();
 
-  // --- row sums: L lanes per row, fixed order, then a butterfly.
-  const int L = p.L;
-  const int lam = tid & (L - 1);
-  for (int i = tid / L; i < p.RB; i += nthr / L) {
-    const int base = (i / p.rpp) * p.P + (i % p.rpp) * p.T;
-    float acc = (lam == 0) ? rowcorr_s[i] : 0.f;
-    for (int tt = lam; tt < p.T; tt += L) acc += part_s[base + tt];
-    for (int off = L >> 1; off > 0; off >>= 1) acc += __shfl_xor(acc, off, L);
-    if (lam == 0 && r0 + i < p.R) p.y[r0 + i] = acc;
+  // --- row sums: one thread per row over its contiguous tile partials.
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    const int i = tid + k * nthr;
+    if (i < p.RB && r0 + i < p.R) {
+      const float* pr = part_s + (i / p.rpp) * p.P + (i % p.rpp) * p.T;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      int tt = 0;
+      for (; tt + 4 <= p.T; tt += 4) { a0 += pr[tt]; a1 += pr[tt + 1]; a2 += pr[tt + 2]; a3 += pr[tt + 3]; }
+      for (; tt < p.T; tt++) a0 += pr[tt];
+      p.y[r0 + i] = ((a0 + a1) + (a2 + a3)) + rowc[k];
+    }
   }
 }
 
@@ -547,6 +641,9 @@ static int env_int(const char* name, int dflt) {
 }
 
 constexpr size_t kLdsBudget = 64 * 1024;
+// Passes of loads in flight per precision (bounded by the VGPRs of a slot:
+// 8 + 4 (M - 2) + pairs dwords).
+constexpr int kDepth[9] = {0, 0, 8, 4, 4, 2, 2, 2, 2};
 constexpr int kMaxWaves = 8;  // matches __launch_bounds__(512) of the GEMV kernel
 
 // LDS carve-up of one workgroup: x, row_ptr slice, group pairs and partials of
@@ -554,7 +651,7 @@ constexpr int kMaxWaves = 8;  // matches __launch_bounds__(512) of the GEMV kern
 static size_t lds_layout(int C, int GU, int nthr, int NP, int rpp, int P, dev::GemvParams* prm) {
   const size_t units = size_t(NP) * P;
   const int RB = NP * rpp;
-  size_t o = (size_t(C) * 2 + 15) & ~size_t(15);
+  size_t o = size_t(C) * 2 + size_t(C / kTileCols) * 16;   // x with 16 B of padding per tile
   if (prm) prm->lds_rp = uint32_t(o);
   o += size_t(RB + 1) * 4;
   o = (o + 15) & ~size_t(15);
@@ -566,68 +663,67 @@ static size_t lds_layout(int C, int GU, int nthr, int NP, int rpp, int P, dev::G
   o += size_t(dev::kEntries) * nthr * 4;
   if (prm) prm->lds_rowcorr = uint32_t(o);
   o += size_t(RB) * 4;
+  o = (o + 15) & ~size_t(15);
+  if (prm) prm->lds_dummy = uint32_t(o);  // 16 B per thread for out-of-range writes
+  o += size_t(nthr) * 16;
   return o;
 }
 
 // Launch shape for one GEMV: k waves per workgroup, rpp rows side by side
-// (rpp * tiles_per_row lanes busy), NP passes, so that every CU gets about the
-// same number of rows.  STAGQ_WAVES / STAGQ_NP override the choice (tuning).
-static bool plan_gemv(const ImageHeader& h, int GU, LaunchCfg* c) {
+// (rpp * tiles_per_row lanes busy), NP passes per workgroup.  Among the shapes
+// that fit LDS, pick the lowest estimated cost on the busiest CU: rounds of
+// workgroups x (passes + 2 of overhead) x lanes, a third more when not all
+// passes fit in flight (NP > depth); ties go to more waves.  STAGQ_WAVES / STAGQ_NP
+// override the choice (tuning).
+static bool plan_gemv(const ImageHeader& h, int GU, int depth, LaunchCfg* c) {
   const int T = h.cols / kTileCols;
   const int R = h.rows;
   const int cus = device_cus();
   const int kmin = std::max(std::max((T + 63) / 64, 1),
                             (h.cols / 8 + dev::kXChunks * 64 - 1) / (dev::kXChunks * 64));
-  auto util = [&](int k) { return double((64 * k / T) * T) / (64.0 * k); };
-  auto grid1 = [&](int k) {  // workgroups at one pass each
-    const int rpp = 64 * k / T;
-    return rpp > 0 ? (R + rpp - 1) / rpp : 0;
-  };
-  int best = 0;
-  const int order[8] = {4, 5, 6, 7, 8, 3, 2, 1};
-  for (int k : order)  // first well-filled shape, preferring about 4 waves
-    if (k >= kmin && util(k) >= 0.97) { best = k; break; }
-  if (!best) {
-    double bu = -1.0;
-    for (int k = kmin; k <= kMaxWaves; k++)
-      if (util(k) > bu + 1e-9) { bu = util(k); best = k; }
+  const int k_env = env_int("STAGQ_WAVES", 0), np_env = env_int("STAGQ_NP", 0);
+  bool found = false;
+  long best_work = 0;
+  int best_k = 0, best_np = 0;
+  bool best_fly = false;
+  for (int k = kmin; k <= kMaxWaves; k++) {
+    if (k_env && k != k_env) continue;
+    const int nthr = 64 * k, rpp = nthr / T;
+    if (rpp < 1) continue;
+    const double util = double(rpp * T) / nthr;
+    if (util < 0.85 && !k_env) continue;
+    const int passes = (R + rpp - 1) / rpp;
+    for (int np = 1; np <= passes; np++) {
+      if (np_env && np != np_env) continue;
+      if (lds_layout(h.cols, GU, nthr, np, rpp, rpp * T, nullptr) > kLdsBudget ||
+          np * rpp + 1 > 2 * nthr)
+        break;
+      const int grid = (passes + np - 1) / np;
+      const bool fly = np <= depth;
+      // lane-passes on the busiest CU, each workgroup paying about two passes
+      // of prologue and epilogue; a third more when passes must wait for slots
+      const long work = long((grid + cus - 1) / cus) * (np + 2) * nthr * (fly ? 3 : 4);
+      const bool better = !found || work < best_work ||
+                          (work == best_work && fly && !best_fly) ||
+                          (work == best_work && fly == best_fly && k > best_k);
+      if (better) { found = true; best_work = work; best_k = k; best_np = np; best_fly = fly; }
+    }
   }
-  if (best > 1 && grid1(best) < cus)  // small matrices: smaller groups to reach every CU
-    for (int k = best - 1; k >= kmin; k--)
-      if (util(k) >= 0.97) { best = k; if (grid1(k) >= cus) break; }
-  const int k = env_int("STAGQ_WAVES", best);
-  if (k < kmin || k > kMaxWaves) return false;
-  const int nthr = 64 * k;
-  const int rpp = nthr / T;
-  if (rpp < 1) return false;
-  const int passes = (R + rpp - 1) / rpp;
-  const int P = rpp * T;
-  auto fits = [&](int np) {
-    return lds_layout(h.cols, GU, nthr, np, rpp, P, nullptr) <= kLdsBudget &&
-           np * rpp + 1 <= 2 * nthr;
-  };
-  // Passes per workgroup: the fewest rounds of workgroups per CU, each round
-  // costing its passes plus about two passes of prologue.
-  int NP = 0;
-  double best_cost = 1e300;
-  for (int np = 1; np <= passes; np++) {
-    if (!fits(np)) break;
-    const int grid = (passes + np - 1) / np;
-    const double cost = double((grid + cus - 1) / cus) * (np + 2.0);
-    if (cost < best_cost - 1e-9) { best_cost = cost; NP = np; }
-    if (grid <= cus) break;
-  }
-  NP = env_int("STAGQ_NP", NP);
-  if (NP < 1 || !fits(NP)) return false;
+  if (!found) return false;
+  const int k = best_k, NP = best_np;
+  const int nthr = 64 * k, rpp = nthr / T, P = rpp * T;
   const int RB = NP * rpp;
   c->waves = k; c->rpp = rpp; c->NP = NP; c->RB = RB;
   c->grid = (R + RB - 1) / RB;
-  int L = 1;
-  while (L < 16 && 2 * L * RB <= nthr) L *= 2;
+  const int L = 16;                      // lanes per row group in the reductions (kLG)
   c->L = L;
+  int rb2 = 1;
+  while (rb2 < RB) rb2 *= 2;
+  c->prm.rb_pow2 = rb2 / 2;
   c->lds = lds_layout(h.cols, GU, nthr, NP, rpp, P, &c->prm);
   c->prm.R = R; c->prm.C = h.cols; c->prm.T = T; c->prm.g = h.group; c->prm.rpp = rpp;
   c->prm.P = P; c->prm.NP = NP; c->prm.RB = RB; c->prm.L = L;
+  if (RB == 1) c->prm.rb_pow2 = 0;
   return true;
 }
 
@@ -639,7 +735,7 @@ static hipError_t launch_gemv(const LaunchCfg& c, hipStream_t st) {
 
 template <int M, int GU>
 static hipError_t launch_gemv_d(const LaunchCfg& c, hipStream_t st) {
-  return launch_gemv<M, GU, (M == 2 ? 4 : 2)>(c, st);
+  return launch_gemv<M, GU, kDepth[M]>(c, st);
 }
 
 template <int M>
@@ -690,7 +786,7 @@ int stagq_pack(const stagq_fields* f, void* dev_buf, size_t dev_bytes, void* hip
         hipStreamSynchronize(s) != hipSuccess)
       st = STAGQ_EHIP;
   }
-  hipHostFree(host);
+  (void)hipHostFree(host);
   if (st != STAGQ_OK) return st;
   return make_handle(h, dev_buf, out);
 }
@@ -722,7 +818,7 @@ int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stre
   if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 4) return STAGQ_EALIGN;
   const int GU = kTileCols / H.group;
   LaunchCfg c;
-  if (!plan_gemv(H, GU, &c)) return STAGQ_ESHAPE;
+  if (!plan_gemv(H, GU, kDepth[bits], &c)) return STAGQ_ESHAPE;
   const uint8_t* b = h->dev;
   c.prm.s0 = b + H.off_s0;
   c.prm.planes = b + H.off_planes;
@@ -759,9 +855,9 @@ int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, in
   if (!layout(rows, cols, group, nbits, 0, &H)) return STAGQ_ESHAPE;
   if (bits < 2 || bits > nbits) return STAGQ_EBITS;
   LaunchCfg c;
-  if (!plan_gemv(H, kTileCols / group, &c)) return STAGQ_ESHAPE;
+  if (!plan_gemv(H, kTileCols / group, kDepth[bits], &c)) return STAGQ_ESHAPE;
   out[0] = c.grid; out[1] = 64 * c.waves; out[2] = c.rpp; out[3] = c.NP; out[4] = c.RB;
-  out[5] = int32_t(c.lds); out[6] = c.L; out[7] = (bits == 2) ? 4 : 2;
+  out[5] = int32_t(c.lds); out[6] = c.L; out[7] = kDepth[bits];
   return STAGQ_OK;
 }
 
