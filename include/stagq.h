@@ -85,8 +85,9 @@ typedef struct {
   int64_t nnz;
   uint64_t image_bytes;      /* size of the packed image */
   /* Algorithmic bytes one GEMV at precision b moves, for b = 2..N (index b;
-   * 0 elsewhere): base stream + planes 3..b + group pairs + side record
-   * (row_ptr, col/q words, values) + x (fp16) + y (fp32). */
+   * 0 elsewhere): base stream + planes 3..b + group pairs + side record (one
+   * 8-byte entry per held-out weight: column, base code, fp16 value, row) + x
+   * (fp16) + y (fp32). */
   uint64_t bytes_read[9];
 } stagq_info;
 

@@ -94,13 +94,14 @@ struct GemvParams {
   const uint8_t* planes;   // plane 3 (plane k at +(k-3)*chunk_bytes)
   const uint8_t* meta;
   const uint8_t* row_ptr;
-  const uint8_t* colq;
-  const uint8_t* val;
+  const uint8_t* side;     // side record, one u64 per entry
   const uint8_t* x;
   float* y;
-  uint32_t chunk_bytes, meta_bytes, colq_bytes, val_bytes, rp_bytes, x_bytes;
-  int32_t R, C, T, g, rpp, P, NP, RB, L, rb_pow2;
-  uint32_t lds_rp, lds_meta, lds_part, lds_corr, lds_rowcorr, lds_dummy;
+  uint32_t chunk_bytes, meta_bytes, side_bytes, rp_bytes, x_bytes;
+  int32_t R, C, T, g, rpp, P, NP, RB;
+  int32_t red;             // tiles per row when rows are reduced in the loop (T | 64), else 0
+  int32_t ppitch;          // LDS floats per row of tile partials (T + 1) when red == 0
+  uint32_t lds_rp, lds_meta, lds_part, lds_corr;
 };
 
 template <int M, int GU>
@@ -240,53 +241,58 @@ __device__ __forceinline__ float tile_partial(const Slot<M, GU>& s, const uint32
   return part;
 }
 
-// Sum over aligned groups of N lanes (N = 8 or 16) with a DPP row_shr
-// inclusive scan; lane N-1 of each group ends up with the group's total.
-// Fixed order, so the result is reproducible.
-template <int SH>
-__device__ __forceinline__ float add_row_shr(float v) {
-  const int xv = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + SH, 0xf, 0xf, true);
-  return v + __builtin_bit_cast(float, xv);
-}
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-  static_assert(N == 8 || N == 16, "DPP row_shr works inside 16-lane rows");
-  v = add_row_shr<1>(v);
-  v = add_row_shr<2>(v);
-  v = add_row_shr<4>(v);
-  if constexpr (N == 16) v = add_row_shr<8>(v);
-  return v;
-}
-constexpr int kLG = 16;  // lanes per row group in the final reductions
-
 // One step of a segmented inclusive scan inside 16-lane rows (DPP row_shr):
-// add the value SH lanes down when it belongs to the same row id r.
+// add the value SH lanes down when it belongs to the same segment r.
 template <int SH>
 __device__ __forceinline__ float seg_step(float v, int r) {
   const int pv = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + SH, 0xf, 0xf, true);
   const int pr = __builtin_amdgcn_update_dpp(-1, r, 0x110 + SH, 0xf, 0xf, false);
   return pr == r ? v + __builtin_bit_cast(float, pv) : v;
 }
+// Carry across 16-lane rows: row_bcast:15 hands lane 15 of row 0/2 to rows
+// 1/3 (row mask 0xa); row_bcast:31 hands lane 31 to rows 2 and 3 (mask 0xc).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float seg_bcast(float v, int r) {
+  const int pv = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xf, false);
+  const int pr = __builtin_amdgcn_update_dpp(-1, r, CTRL, ROWMASK, 0xf, false);
+  return pr == r ? v + __builtin_bit_cast(float, pv) : v;
+}
+// Segmented inclusive scan over the 64 lanes of a wave (segment ids sorted by
+// lane): afterwards the last lane of every segment holds the segment's sum.
+__device__ __forceinline__ float seg_scan64(float v, int r) {
+  v = seg_step<1>(v, r);
+  v = seg_step<2>(v, r);
+  v = seg_step<4>(v, r);
+  v = seg_step<8>(v, r);
+  v = seg_bcast<0x142, 0xa>(v, r);
+  v = seg_bcast<0x143, 0xc>(v, r);
+  return v;
+}
 
 // LDS column index of x: every 128-column tile is followed by 16 bytes of
-// padding, so lanes reading their own tiles hit different banks.
+// padding (conflict-free row reads in the correction phase).
 __device__ __forceinline__ int xcol(int c) { return c + ((c >> 7) << 3); }
+
+__device__ __forceinline__ uint64_t ld64side(rsrc_t r, uint32_t off) {
+  const u32x2 v = ld64(r, off);
+  return uint64_t(v[0]) | (uint64_t(v[1]) << 32);
+}
 
 template <int M, int GU, int D>
 __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
-  int32_t* rp = reinterpret_cast<int32_t*>(lds + p.lds_rp);
+  int32_t* rp_s = reinterpret_cast<int32_t*>(lds + p.lds_rp);
   uint32_t* meta_s = reinterpret_cast<uint32_t*>(lds + p.lds_meta);
   float* part_s = reinterpret_cast<float*>(lds + p.lds_part);
   float* corr_s = reinterpret_cast<float*>(lds + p.lds_corr);
-  float* rowcorr_s = reinterpret_cast<float*>(lds + p.lds_rowcorr);
 
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int r0 = blockIdx.x * p.RB;
   const int rip = tid / p.T;            // row slot within a pass
   const int t = tid - rip * p.T;        // tile column
   const bool act = rip < p.rpp;
+  const int rows_here = min(p.RB, p.R - r0);
 
   const rsrc_t rA = mk(p.s0, p.chunk_bytes);
   const rsrc_t rB = mk(p.s0 + p.chunk_bytes, p.chunk_bytes);
@@ -296,16 +302,18 @@ __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
   const rsrc_t rMeta = mk(p.meta, p.meta_bytes);
   const rsrc_t rX = mk(p.x, p.x_bytes);
   const rsrc_t rRp = mk(p.row_ptr, p.rp_bytes);
-  const rsrc_t rCq = mk(p.colq, p.colq_bytes);
-  const rsrc_t rVal = mk(p.val, p.val_bytes);
+  const rsrc_t rSide = mk(p.side, p.side_bytes);
 
-  // --- prologue: row_ptr and x first (needed first), then D passes of weights.
-  uint32_t rpv[2];  // row_ptr[r0 .. r0 + RB], clamped at R (RB + 1 <= 2 * nthr)
+  // --- prologue.  Load order = arrival order: the workgroup's side-record
+  //     range, this lane's x slice, x chunks and row_ptr for the LDS copies used
+  //     at the end, then every pass of weights.  No barrier stands between the
+  //     loads and the first pass.
+  const uint32_t e0u = ld32(rRp, uint32_t(r0) * 4u);
+  const uint32_t e1u = ld32(rRp, uint32_t(r0 + rows_here) * 4u);
+  u32x4 xq[16];
+  const uint32_t xbase = uint32_t(act ? t : 0) * 256u;
 #pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int j = tid + i * nthr;
-    rpv[i] = ld32(rRp, j <= p.RB ? uint32_t(min(r0 + j, p.R)) * 4u : kOOB);
-  }
+  for (int k = 0; k < 16; k++) xq[k] = ld128(rX, xbase + 16u * k);
   const int xchunks = p.C >> 3;
   u32x4 xv[kXChunks];
 #pragma unroll
@@ -313,51 +321,46 @@ __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
     const int ci = tid + i * nthr;
     xv[i] = ld128(rX, ci < xchunks ? uint32_t(ci) * 16u : kOOB);
   }
-  __builtin_amdgcn_sched_barrier(0);     // row_ptr and x stay ahead of the weight loads
-  // Only the first pass is requested before x: x and row_ptr queue behind
-  // whatever is in flight, so the rest of the weights follow the barrier.
-  Slot<M, GU> sl[D];
-  {
-    const int row = r0 + rip;
-    issue(sl[0], rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && 0 < p.NP && row < p.R);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // The LDS writes below are unconditional (out-of-range slots go to a per-thread
-  // scratch area): a load whose value is only used under a branch would be sunk
-  // into it and waited on after the weight loads, delaying the barrier until
-  // the first D passes of weights had arrived.
-  uint8_t* dummy = lds + p.lds_dummy + tid * 16;
+  uint32_t rpv[2];                       // row_ptr[r0 + j], j = tid, tid + nthr (<= rows_here)
 #pragma unroll
   for (int i = 0; i < 2; i++) {
     const int j = tid + i * nthr;
-    *reinterpret_cast<int32_t*>(j <= p.RB ? reinterpret_cast<uint8_t*>(rp + j) : dummy) = int32_t(rpv[i]);
+    rpv[i] = ld32(rRp, j <= rows_here ? uint32_t(r0 + j) * 4u : kOOB);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  Slot<M, GU> sl[D];
 #pragma unroll
-  for (int i = 0; i < kXChunks; i++) {
-    const int ci = tid + i * nthr;
-    *reinterpret_cast<u32x4*>(ci < xchunks ? reinterpret_cast<uint8_t*>(xs + xcol(ci * 8)) : dummy) = xv[i];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 1; i < D; i++) {          // slot by slot: pass i's loads complete first
+  for (int i = 0; i < D; i++) {          // slot by slot: pass i's loads complete first
     const int row = r0 + i * p.rpp + rip;
     issue(sl[i], rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && i < p.NP && row < p.R);
     __builtin_amdgcn_sched_barrier(0);
   }
-  const int e0 = rp[0], e1 = rp[p.RB];
+  // LDS copies of x and row_ptr for the end (read after the loop's barrier).
+  // The writes are unconditional (spare ones land in pad slots) so the loads
+  // above are never sunk into a branch and waited on late.
+#pragma unroll
+  for (int i = 0; i < kXChunks; i++) {
+    const int ci = tid + i * nthr;
+    *reinterpret_cast<u32x4*>(xs + (ci < xchunks ? xcol(ci * 8) : xcol(p.C))) = xv[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int j = tid + i * nthr;
+    rp_s[j <= rows_here ? j : p.RB + 1] = int32_t(rpv[i]);
+  }
+  const int e0 = int(e0u), e1 = int(e1u);
 
   // --- x slice of this lane's tile as permuted fp16 pairs; per-group sum(x).
   uint32_t xp[64];
   float sx[GU];
 #pragma unroll
   for (int gi = 0; gi < GU; gi++) sx[gi] = 0.f;
-  const uint16_t* xt = xs + xcol((act ? t : 0) * 128);
 #pragma unroll
   for (int d = 0; d < 4; d++) {
     uint32_t xr[64];
 #pragma unroll
     for (int q4 = 0; q4 < 4; q4++) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(xt + 32 * d + 8 * q4);
+      const u32x4 v = xq[4 * d + q4];
       xr[16 * d + 4 * q4 + 0] = v[0]; xr[16 * d + 4 * q4 + 1] = v[1];
       xr[16 * d + 4 * q4 + 2] = v[2]; xr[16 * d + 4 * q4 + 3] = v[3];
     }
@@ -382,21 +385,35 @@ __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
     }
   }
 
-  // --- main loop over passes, D passes of loads in flight.  After the first
-  //     pass, while later passes stream in, the workgroup's first side-record
-  //     entries are fetched and their rows found (branch-free binary search,
-  //     all entries in lockstep).
-  uint32_t cq[kEntries], pv[kEntries];
-  int erow[kEntries];
-  // One pass: its tile partial and group pairs go to LDS, then its slot is
-  // reloaded with pass + D (out of range -> zeros, no memory traffic), so the
-  // number of loads every wait counts is the same on every path.
+  // --- main loop.  A pass: the lane's tile partial; when a row's tiles are a
+  //     power-of-two group of lanes inside one wave the row is summed at once
+  //     with DPP and one value per row goes to LDS, otherwise one value per
+  //     tile.  The slot is then reloaded with pass + D (out of range -> zeros,
+  //     no traffic), which keeps every wait count path-independent.
+  const int lane = tid & 63;
+  uint64_t ent[kEntries];
   auto step_pass = [&](Slot<M, GU>& sl_i, int pass) {
     if (pass < p.NP) {
-      const float part = tile_partial<M, GU>(sl_i, xp, sx);
+      float part = tile_partial<M, GU>(sl_i, xp, sx);
+      if (p.red > 0) {
+        // Every DPP step runs on all lanes (a lane reading a masked-off
+        // neighbour would see 0); groups narrower than a 16-lane row then
+        // keep the sum only where the source lane is in their own group.
+        const int T = p.red;
+        const int li = lane & (T - 1);
+        float v;
+        if (T >= 2) { v = seg_step<1>(part, 0); part = li >= 1 ? v : part; }
+        if (T >= 4) { v = seg_step<2>(part, 0); part = li >= 2 ? v : part; }
+        if (T >= 8) { v = seg_step<4>(part, 0); part = li >= 4 ? v : part; }
+        if (T >= 16) part = seg_step<8>(part, 0);
+        if (T >= 32) part = seg_bcast<0x142, 0xa>(part, T == 32 ? (lane >> 5) : 0);
+        if (T >= 64) part = seg_bcast<0x143, 0xc>(part, 0);
+        if (li == T - 1 && act) part_s[pass * p.rpp + rip] = part;
+      } else if (act) {
+        part_s[(pass * p.rpp + rip) * p.ppitch + t] = part;
+      }
       if (act) {
         const int slot = pass * p.P + tid;
-        part_s[slot] = part;
 #pragma unroll
         for (int gi = 0; gi < GU; gi++) meta_s[slot * GU + gi] = sl_i.meta[gi];
       }
@@ -405,9 +422,8 @@ __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
     const int row = r0 + np * p.rpp + rip;
     issue(sl_i, rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && np < p.NP && row < p.R);
   };
-  // The first D passes in straight-line code; after the first of them, while
-  // the others stream in, fetch this workgroup's first side-record entries and
-  // find their rows (branch-free binary search, all entries in lockstep).
+  // The first D passes in straight-line code; after the first, fetch this
+  // workgroup's first side-record entries (one u64 each) for the end.
 #pragma unroll
   for (int i = 0; i < D; i++) {
     step_pass(sl[i], i);
@@ -415,118 +431,80 @@ __global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
 #pragma unroll
       for (int j = 0; j < kEntries; j++) {
         const int e = e0 + tid + j * nthr;
-        const bool ok = e < e1;
-        cq[j] = ld32(rCq, ok ? uint32_t(e) * 4u : kOOB);
-        pv[j] = ld16(rVal, ok ? uint32_t(e) * 2u : kOOB);
-        erow[j] = 0;
-      }
-      // rp[RB] = e1 > e, so clamping the probe at RB keeps the reads unconditional.
-      for (int step = p.rb_pow2; step > 0; step >>= 1) {
-        int probe[kEntries];
-#pragma unroll
-        for (int j = 0; j < kEntries; j++) probe[j] = rp[min(erow[j] + step, p.RB)];
-#pragma unroll
-        for (int j = 0; j < kEntries; j++)
-          if (probe[j] <= e0 + tid + j * nthr) erow[j] += step;
+        ent[j] = ld64side(rSide, e < e1 ? uint32_t(e) * 8u : kOOB);
       }
     }
   }
-  // Remaining passes (workgroups with more passes than loads in flight).
   for (int pb = D; pb < p.NP; pb += D) {
 #pragma unroll
     for (int i = 0; i < D; i++) step_pass(sl[i], pb + i);
   }
   __syncthreads();
 
-  // --- side-record corrections (P - W_main) x_c, W_main = lo + s (q - 1/2 + 2^(1-M)).
-  //     Entries are processed in chunks of kEntries * nthr in entry order; within
-  //     each block of 64 consecutive entries (one wave) a segmented inclusive scan
-  //     by row leaves, at the last entry of every row run, that run's sum.  Each
-  //     row then adds one value per 64-entry block it touches.  Fixed order.
+  // --- side-record corrections (P - W_main) x_c, W_main = lo + s (q - 1/2 + 2^(1-M)),
+  //     in chunks of kEntries * nthr entries in entry order.  Within each block
+  //     of 64 consecutive entries (one wave) a segmented scan by row leaves, at
+  //     the last entry of every row run, that run's sum; a row then adds one
+  //     value per 64-entry block it touches.  Fixed order throughout.
   constexpr float kHeld = -0.5f + 1.0f / float(1 << (M - 1));
   const int chunk = kEntries * nthr;
-  const int lane = tid & 63;
-  auto correction = [&](uint32_t colq, uint32_t pbits, int rloc) -> float {
-    const int c = int(colq & 0x3fffffffu);
-    const int q = int(colq >> 30);
+  auto row_of = [&](uint64_t ev) -> int {   // row within the workgroup
+    return int((uint32_t(ev >> 48) - uint32_t(r0)) & 0xffffu);
+  };
+  auto correction = [&](uint64_t ev) -> float {
+    const int c = min(int(uint32_t(ev) & 0x3fffffffu), p.C - 1);
+    const int q = int(uint32_t(ev) >> 30);
+    const int rloc = min(row_of(ev), p.RB - 1);
     const int slot = (rloc / p.rpp) * p.P + (rloc % p.rpp) * p.T + (c >> 7);
     const int gi = (c & 127) / p.g;
     const uint32_t mw = meta_s[slot * GU + gi];
     const float lo = h2f(mw & 0xffffu), st = h2f(mw >> 16);
     const float wmain = lo + st * (float(q) + kHeld);
-    return (h2f(pbits) - wmain) * h2f(xs[xcol(c)]);
-  };
-  // Segmented inclusive scan over the 64 lanes: inside each 16-lane row with DPP
-  // shifts 1, 2, 4, 8, then carries from the last lane of the row before
-  // (covering 16 more lanes) and of the row two before (32 more), each added
-  // only when it belongs to the same row id (row ids are sorted by lane).
-  auto seg_scan = [&](float v, int r) -> float {
-    v = seg_step<1>(v, r);
-    v = seg_step<2>(v, r);
-    v = seg_step<4>(v, r);
-    v = seg_step<8>(v, r);
-    const int rs = lane & ~15;
-    {
-      const int src = rs > 0 ? rs - 1 : lane;
-      const float pv = __shfl(v, src, 64);
-      const int pr = __shfl(r, src, 64);
-      if (rs > 0 && pr == r) v += pv;
-    }
-    {
-      const int src = rs > 16 ? rs - 17 : lane;
-      const float pv = __shfl(v, src, 64);
-      const int pr = __shfl(r, src, 64);
-      if (rs > 16 && pr == r) v += pv;
-    }
-    return v;
+    return (h2f(uint32_t(ev >> 32) & 0xffffu) - wmain) * h2f(xs[xcol(c)]);
   };
   float rowc[2] = {0.f, 0.f};             // this thread's rows: tid and tid + nthr
   for (int ce = e0; ce < e1; ce += chunk) {
-    float sv[kEntries];
-    if (ce == e0) {
-#pragma unroll
-      for (int j = 0; j < kEntries; j++) {
-        const bool ok = e0 + tid + j * nthr < e1;
-        sv[j] = seg_scan(correction(cq[j], pv[j], erow[j]), ok ? erow[j] : p.RB);
-      }
-    } else {                              // rare: more entries than one prefetched chunk
+    if (ce > e0) {                        // rare: more entries than one prefetched chunk
       __syncthreads();                    // previous chunk consumed
 #pragma unroll
       for (int j = 0; j < kEntries; j++) {
         const int e = ce + tid + j * nthr;
-        const bool ok = e < e1;
-        int lo = 0;
-        for (int step = p.rb_pow2; step > 0; step >>= 1)
-          if (rp[min(lo + step, p.RB)] <= e) lo += step;
-        const float cv = correction(ld32(rCq, ok ? uint32_t(e) * 4u : kOOB),
-                                    ld16(rVal, ok ? uint32_t(e) * 2u : kOOB), lo);
-        sv[j] = seg_scan(cv, ok ? lo : p.RB);
+        ent[j] = ld64side(rSide, e < e1 ? uint32_t(e) * 8u : kOOB);
       }
     }
 #pragma unroll
-    for (int j = 0; j < kEntries; j++) corr_s[tid + j * nthr] = sv[j];
+    for (int j = 0; j < kEntries; j++) {
+      const bool ok = ce + tid + j * nthr < e1;
+      corr_s[tid + j * nthr] = seg_scan64(correction(ent[j]), ok ? row_of(ent[j]) : p.RB);
+    }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 2; k++) {
       const int i = tid + k * nthr;
-      if (i < p.RB) {
-        const int a = max(rp[i], ce) - ce, b = min(rp[i + 1], ce + chunk) - ce;
+      if (i < rows_here) {
+        const int a = max(rp_s[i], ce) - ce, b = min(rp_s[i + 1], ce + chunk) - ce;
         for (int q = a; q < b; q = (q | 63) + 1) rowc[k] += corr_s[min(b, (q | 63) + 1) - 1];
       }
     }
   }
 
-  // --- row sums: one thread per row over its contiguous tile partials.
+  // --- row sums: one thread per row.
 #pragma unroll
   for (int k = 0; k < 2; k++) {
     const int i = tid + k * nthr;
-    if (i < p.RB && r0 + i < p.R) {
-      const float* pr = part_s + (i / p.rpp) * p.P + (i % p.rpp) * p.T;
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-      int tt = 0;
-      for (; tt + 4 <= p.T; tt += 4) { a0 += pr[tt]; a1 += pr[tt + 1]; a2 += pr[tt + 2]; a3 += pr[tt + 3]; }
-      for (; tt < p.T; tt++) a0 += pr[tt];
-      p.y[r0 + i] = ((a0 + a1) + (a2 + a3)) + rowc[k];
+    if (i < rows_here) {
+      float acc;
+      if (p.red > 0) {
+        acc = part_s[i];
+      } else {
+        const float* pr = part_s + i * p.ppitch;
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+        int tt = 0;
+        for (; tt + 4 <= p.T; tt += 4) { a0 += pr[tt]; a1 += pr[tt + 1]; a2 += pr[tt + 2]; a3 += pr[tt + 3]; }
+        for (; tt < p.T; tt++) a0 += pr[tt];
+        acc = (a0 + a1) + (a2 + a3);
+      }
+      p.y[r0 + i] = acc + rowc[k];
     }
   }
 }
@@ -646,28 +624,30 @@ constexpr size_t kLdsBudget = 64 * 1024;
 constexpr int kDepth[9] = {0, 0, 8, 4, 4, 2, 2, 2, 2};
 constexpr int kMaxWaves = 8;  // matches __launch_bounds__(512) of the GEMV kernel
 
-// LDS carve-up of one workgroup: x, row_ptr slice, group pairs and partials of
-// every tile it owns, side-record corrections, per-row correction sums.
-static size_t lds_layout(int C, int GU, int nthr, int NP, int rpp, int P, dev::GemvParams* prm) {
+// LDS carve-up of one workgroup: padded x (plus one spare 16-byte slot),
+// row_ptr of its rows (plus a spare slot), group pairs of every tile it owns,
+// row (or tile) partials, and one chunk of scanned side-record corrections.
+static size_t lds_layout(int C, int GU, int nthr, int NP, int rpp, int P, int T, bool red,
+                         dev::GemvParams* prm) {
   const size_t units = size_t(NP) * P;
   const int RB = NP * rpp;
-  size_t o = size_t(C) * 2 + size_t(C / kTileCols) * 16;   // x with 16 B of padding per tile
+  size_t o = size_t(C) * 2 + size_t(C / kTileCols) * 16 + 16;
   if (prm) prm->lds_rp = uint32_t(o);
-  o += size_t(RB + 1) * 4;
+  o += size_t(RB + 2) * 4;
   o = (o + 15) & ~size_t(15);
   if (prm) prm->lds_meta = uint32_t(o);
   o += units * 4 * GU;
   if (prm) prm->lds_part = uint32_t(o);
-  o += units * 4;
+  o += red ? size_t(RB) * 4 : size_t(RB) * (T + 1) * 4;
+  o = (o + 15) & ~size_t(15);
   if (prm) prm->lds_corr = uint32_t(o);
   o += size_t(dev::kEntries) * nthr * 4;
-  if (prm) prm->lds_rowcorr = uint32_t(o);
-  o += size_t(RB) * 4;
-  o = (o + 15) & ~size_t(15);
-  if (prm) prm->lds_dummy = uint32_t(o);  // 16 B per thread for out-of-range writes
-  o += size_t(nthr) * 16;
   return o;
 }
+
+// Rows are summed inside the loop when a row's tiles form a power-of-two group
+// of lanes within one wave.
+static bool row_reduce(int T) { return T <= 64 && (T & (T - 1)) == 0; }
 
 // Launch shape for one GEMV: k waves per workgroup, rpp rows side by side
 // (rpp * tiles_per_row lanes busy), NP passes per workgroup.  Among the shapes
@@ -695,7 +675,7 @@ static bool plan_gemv(const ImageHeader& h, int GU, int depth, LaunchCfg* c) {
     const int passes = (R + rpp - 1) / rpp;
     for (int np = 1; np <= passes; np++) {
       if (np_env && np != np_env) continue;
-      if (lds_layout(h.cols, GU, nthr, np, rpp, rpp * T, nullptr) > kLdsBudget ||
+      if (lds_layout(h.cols, GU, nthr, np, rpp, rpp * T, T, row_reduce(T), nullptr) > kLdsBudget ||
           np * rpp + 1 > 2 * nthr)
         break;
       const int grid = (passes + np - 1) / np;
@@ -715,15 +695,13 @@ static bool plan_gemv(const ImageHeader& h, int GU, int depth, LaunchCfg* c) {
   const int RB = NP * rpp;
   c->waves = k; c->rpp = rpp; c->NP = NP; c->RB = RB;
   c->grid = (R + RB - 1) / RB;
-  const int L = 16;                      // lanes per row group in the reductions (kLG)
-  c->L = L;
-  int rb2 = 1;
-  while (rb2 < RB) rb2 *= 2;
-  c->prm.rb_pow2 = rb2 / 2;
-  c->lds = lds_layout(h.cols, GU, nthr, NP, rpp, P, &c->prm);
+  c->L = 0;
+  const bool red = row_reduce(T);
+  c->lds = lds_layout(h.cols, GU, nthr, NP, rpp, P, T, red, &c->prm);
   c->prm.R = R; c->prm.C = h.cols; c->prm.T = T; c->prm.g = h.group; c->prm.rpp = rpp;
-  c->prm.P = P; c->prm.NP = NP; c->prm.RB = RB; c->prm.L = L;
-  if (RB == 1) c->prm.rb_pow2 = 0;
+  c->prm.P = P; c->prm.NP = NP; c->prm.RB = RB;
+  c->prm.red = red ? T : 0;
+  c->prm.ppitch = T + 1;
   return true;
 }
 
@@ -824,14 +802,12 @@ int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stre
   c.prm.planes = b + H.off_planes;
   c.prm.meta = b + H.off_meta;
   c.prm.row_ptr = b + H.off_rowptr;
-  c.prm.colq = b + H.off_colq;
-  c.prm.val = b + H.off_val;
+  c.prm.side = b + H.off_side;
   c.prm.x = static_cast<const uint8_t*>(x);
   c.prm.y = y;
   c.prm.chunk_bytes = uint32_t(H.bytes_s0_chunk);
   c.prm.meta_bytes = uint32_t(H.bytes_meta);
-  c.prm.colq_bytes = uint32_t(H.nnz * 4);
-  c.prm.val_bytes = uint32_t(H.nnz * 2);
+  c.prm.side_bytes = uint32_t(H.nnz * 8);
   c.prm.rp_bytes = uint32_t((H.rows + 1) * 4);
   c.prm.x_bytes = uint32_t(H.cols * 2);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);

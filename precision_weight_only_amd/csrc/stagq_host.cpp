@@ -80,10 +80,13 @@ int validate_fields(const stagq_fields* f, ImageHeader* h) {
   return STAGQ_OK;
 }
 
+// Bytes one GEMV moves: base stream, planes 3..bits, group pairs, the side
+// record (8 B per entry), x and y.  (row_ptr is read only at workgroup
+// boundaries, a few KB, and is not counted.)
 uint64_t bytes_read(const ImageHeader& h, int bits) {
   const uint64_t n = uint64_t(h.rows) * h.cols;
-  return n * 2 / 8 + n * uint64_t(bits - 2) / 8 + h.bytes_meta + uint64_t(h.rows + 1) * 4 +
-         uint64_t(h.nnz) * 6 + uint64_t(h.cols) * 2 + uint64_t(h.rows) * 4;
+  return n * 2 / 8 + n * uint64_t(bits - 2) / 8 + h.bytes_meta + uint64_t(h.nnz) * 8 +
+         uint64_t(h.cols) * 2 + uint64_t(h.rows) * 4;
 }
 
 // ----------------------------------------------------------------- pack ----
@@ -175,13 +178,12 @@ int stagq_pack_host(const stagq_fields* f, void* dst, size_t dst_bytes) {
   uint32_t* meta = reinterpret_cast<uint32_t*>(img + h.off_meta);
   for (int64_t i = 0; i < R * G; i++) meta[i] = uint32_t(f->lo[i]) | (uint32_t(f->s[i]) << 16);
   memcpy(img + h.off_rowptr, f->row_ptr, size_t(R + 1) * 4);
-  uint32_t* colq = reinterpret_cast<uint32_t*>(img + h.off_colq);
-  uint16_t* val = reinterpret_cast<uint16_t*>(img + h.off_val);
+  uint64_t* side = reinterpret_cast<uint64_t*>(img + h.off_side);
   for (int64_t r = 0; r < R; r++)
     for (int64_t e = f->row_ptr[r]; e < f->row_ptr[r + 1]; e++) {
-      const uint32_t c = uint32_t(f->col[e]);
-      colq[e] = c | (uint32_t(f->q[r * f->cols + c]) << 30);
-      val[e] = f->val[e];
+      const uint64_t c = uint64_t(uint32_t(f->col[e]));
+      side[e] = c | (uint64_t(f->q[r * f->cols + c]) << 30) | (uint64_t(f->val[e]) << 32) |
+                (uint64_t(r & 0xffff) << 48);
     }
   return STAGQ_OK;
 }
@@ -232,11 +234,10 @@ int stagq_unpack_host(const void* image, size_t image_bytes, stagq_info* shape, 
     if (s) s[i] = uint16_t(meta[i] >> 16);
   }
   if (row_ptr) memcpy(row_ptr, img + h.off_rowptr, size_t(h.rows + 1) * 4);
-  const uint32_t* colq = reinterpret_cast<const uint32_t*>(img + h.off_colq);
-  const uint16_t* v = reinterpret_cast<const uint16_t*>(img + h.off_val);
+  const uint64_t* side = reinterpret_cast<const uint64_t*>(img + h.off_side);
   for (int64_t e = 0; e < h.nnz; e++) {
-    if (col) col[e] = int32_t(colq[e] & 0x3fffffffu);
-    if (val) val[e] = v[e];
+    if (col) col[e] = int32_t(side[e] & 0x3fffffffu);
+    if (val) val[e] = uint16_t(side[e] >> 32);
   }
   return STAGQ_OK;
 }

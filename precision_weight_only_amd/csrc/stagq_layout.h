@@ -10,8 +10,11 @@
 //   base stream S0   2 chunks x U tiles x 16 B   (2 bits per weight)
 //   plane k = 3..N   1 chunk  x U tiles x 16 B   (1 bit per weight), plane-major
 //   pairs            rows * (cols / g) x 4 B     (fp16 lo | fp16 s << 16)
-//   side record      row_ptr [rows+1] i32, colq [nnz] u32 (col | q << 30),
-//                    val [nnz] fp16 (the recorded weight)
+//   side record      row_ptr [rows+1] i32, and per entry one u64:
+//                    bits 0..29 col, 30..31 base code q at (row, col),
+//                    32..47 the recorded weight (fp16), 48..63 row mod 2^16
+//                    (a workgroup owning fewer than 2^16 consecutive rows
+//                    recovers the full row from its first row)
 //
 // Plane order puts the base first and the planes in order of k, so a read at
 // precision M touches S0 and planes 3..M only (the prefix property of the
@@ -33,7 +36,7 @@ namespace stagq {
 constexpr int kTileCols = 128;
 constexpr int kChunkBytes = 16;
 constexpr uint32_t kImageMagic = 0x51474153u;  // "SAGQ"
-constexpr uint32_t kImageVersion = 1;
+constexpr uint32_t kImageVersion = 2;
 constexpr int kMaxBits = 8;
 
 struct ImageHeader {           // first 256 bytes of an image
@@ -41,7 +44,7 @@ struct ImageHeader {           // first 256 bytes of an image
   int32_t rows, cols, group, nbits;
   int64_t nnz;
   int64_t tiles;               // U = rows * cols / 128
-  uint64_t off_s0, off_planes, off_meta, off_rowptr, off_colq, off_val, total;
+  uint64_t off_s0, off_planes, off_meta, off_rowptr, off_side, off_unused, total;
   uint64_t bytes_s0_chunk;     // U * 16
   uint64_t bytes_plane;        // U * 16
   uint64_t bytes_meta;         // rows * cols / group * 4
@@ -58,7 +61,7 @@ inline bool layout(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int
   if (rows < 0 || cols <= 0 || cols % kTileCols != 0) return false;
   if (group != 32 && group != 64 && group != 128) return false;
   if (nbits < 2 || nbits > kMaxBits) return false;
-  if (nnz < 0 || nnz >= (int64_t(1) << 31)) return false;
+  if (nnz < 0 || nnz >= (int64_t(1) << 28)) return false;  // side record below 2 GiB
   if (cols >= (1 << 30)) return false;
   *h = ImageHeader{};
   h->magic = kImageMagic;
@@ -75,8 +78,8 @@ inline bool layout(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int
   h->off_planes = o;  o = align256(o + uint64_t(nbits - 2) * h->bytes_plane);
   h->off_meta = o;    o = align256(o + h->bytes_meta);
   h->off_rowptr = o;  o = align256(o + uint64_t(rows + 1) * 4);
-  h->off_colq = o;    o = align256(o + uint64_t(nnz) * 4);
-  h->off_val = o;     o = align256(o + uint64_t(nnz) * 2);
+  h->off_side = o;    o = align256(o + uint64_t(nnz) * 8);
+  h->off_unused = o;
   h->total = o;
   return true;
 }

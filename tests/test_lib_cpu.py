@@ -104,7 +104,7 @@ def test_bytes_read_model():
                                 None, None, None, None, None, None, None)
     n = 32 * 1024
     for M in (2, 3, 4):
-        want = n * M // 8 + 32 * 8 * 4 + 33 * 4 + F.nnz * 6 + 1024 * 2 + 32 * 4
+        want = n * M // 8 + 32 * 8 * 4 + F.nnz * 8 + 1024 * 2 + 32 * 4   # side entry: one u64
         assert info.bytes_read[M] == want
     assert U["nnz"] == F.nnz
 
