@@ -19,8 +19,8 @@
  * reconstruction is (1 - m) * W_main + P (Eq. 4).
  *
  * Matrices are rows (output channels) x cols (input channels); a group is g
- * consecutive columns of one row.  Supported: cols a positive multiple of 128,
- * g in {32, 64, 128}, 2 <= N <= 8, every device stream below 2 GiB.
+ * consecutive columns of one row.  Supported: cols a positive multiple of 128
+ * up to 32768, g in {32, 64, 128}, 2 <= N <= 8, every device stream below 2 GiB.
  *
  * Conventions for every call:
  *   - Return value: STAGQ_OK (0) or a negative STAGQ_E* status.  Arguments are
@@ -145,9 +145,10 @@ int stagq_decode_codes(stagq_handle h, int bits, uint8_t* codes, void* hip_strea
 /*
  * Launch shape the GEMV uses for a matrix of this shape at precision bits (on
  * the current device, or assuming 256 compute units when none is present):
- * out[0] workgroups, out[1] threads per workgroup, out[2] rows per pass,
- * out[3] passes, out[4] rows per workgroup, out[5] LDS bytes, out[6] lanes per
- * row in the final reduction, out[7] passes of loads in flight.  out is host
+ * out[0] workgroups (one per 16-row block), out[1] threads per workgroup,
+ * out[2] waves per workgroup, out[3] steps per wave (a step is 16 rows x 4
+ * tile columns of 128), out[4] rows per workgroup, out[5] LDS bytes, out[6]
+ * reserved (0), out[7] steps of loads in flight per wave.  out is host
  * int32[8].  Pure host logic.
  */
 int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int bits,

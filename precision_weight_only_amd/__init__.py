@@ -65,8 +65,8 @@ def plan_gemv(rows: int, cols: int, group: int, nbits: int, bits: int) -> Dict[s
     out = (C.c_int32 * 8)()
     check(lib().stagq_plan_gemv(rows, cols, group, nbits, bits, C.cast(out, C.c_void_p)),
           "stagq_plan_gemv")
-    keys = ("grid", "threads", "rows_per_pass", "passes", "rows_per_group", "lds_bytes",
-            "lanes_per_row", "depth")
+    keys = ("grid", "threads", "waves", "steps_per_wave", "rows_per_group", "lds_bytes",
+            "reserved", "depth")
     return dict(zip(keys, list(out)))
 
 

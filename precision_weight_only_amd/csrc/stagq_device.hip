@@ -2,29 +2,33 @@
 // batch-one GEMV, the code-dump kernel, and their host dispatch.
 //
 // GEMV design (one launch per call):
-//  * A lane owns one 128-column tile of one row.  A workgroup of k waves runs
-//    `rpp` rows side by side (rpp * tiles_per_row <= 64k lanes) for NP passes,
-//    so it owns RB = NP * rpp consecutive rows and a contiguous range of every
-//    stream.  All global loads go through buffer resources: out-of-range lanes
-//    read zeros instead of faulting.
-//  * x (fp16) is staged once into LDS, then each lane keeps the 128 values of
-//    its tile in 64 VGPRs as fp16 pairs, permuted to match the bit placement of
-//    the packed stream (see stagq_layout.h).
-//  * Per pass a lane fetches its tile's base stream (2 x dwordx4), planes 3..M
-//    (1 x dwordx4 each) and group pairs, D passes ahead of use.
+//  * A workgroup owns a block of 16 rows (whole rows, so no atomics and no
+//    second pass).  A wave step covers 16 rows x 4 consecutive tile columns:
+//    lane = (tile column within the four) * 16 + row.  The S waves of the
+//    workgroup split the row's groups of four tile columns between them.
+//  * Per step a wave issues one contiguous 1 KB dwordx4 load per stream chunk
+//    (base stream, planes 3..M) and one load of the group pairs, D steps ahead
+//    of use.  All global loads of the streams go through buffer resources:
+//    out-of-range offsets read zeros instead of faulting.
+//  * x is staged once per workgroup in LDS (each tile padded by 16 bytes so
+//    the four tile columns of a step fall in different banks) together with
+//    sum(x) per group; a step reads its tile's x one 32-column quarter ahead
+//    of use.
 //  * Decode: the codes of two weights are isolated into the low mantissa bits
 //    of the two fp16 halves of a register (fp16 subnormals, value u * 2^-24,
-//    exact), so one v_dot2_f32_f16 multiplies two codes by two x values and
-//    accumulates in fp32.  For M >= 3 the planes are first merged with the base
-//    codes into 4-bit codes (Eq. 8) with shifts and bit-field inserts.
-//  * Per tile and group: partial = s_M * sum(u x) + lo_M * sum(x) (the affine
-//    collapse of Eq. 10 summed over the group), in fp32.
-//  * Side record (Eq. 4): each entry contributes (P - W_main) x_c, where the
-//    main stream decodes W_main = lo + s (q - 1/2 + 2^(1-M)) there because its
-//    planes are zero.  Entries are prefetched in the prologue and corrected at
-//    the end from LDS copies of the group pairs and x.
-//  * Row sums: fixed-order sums of the tile partials and the row's corrections
-//    (no atomics), so y is bitwise reproducible for a given shape and M.
+//    exact), so one v_dot2_f32_f16 multiplies two codes by the natural x pair
+//    (x[2i], x[2i+1]) and accumulates in fp32.  For M >= 3 the planes are first
+//    merged with the base codes into 4-bit codes (Eq. 8) with shifts and
+//    bit-field inserts.
+//  * Per group: s_M * sum(u x) + lo_M * sum(x) (the affine collapse of Eq. 10
+//    summed over the group), in fp32.
+//  * Side record (Eq. 4): each entry carries a = P - lo - s (q - 1/2) and s, so
+//    its contribution (P - W_main) x_c = (a - s 2^(1-M)) x_c needs only x_c
+//    (the main stream decodes W_main = lo + s (q - 1/2 + 2^(1-M)) there because
+//    its planes are zero).  A row's entries are dealt round-robin to the 4 S
+//    lanes that hold the row, prefetched at the start, applied after the loop.
+//  * Row sums: the 4 S lane partials of a row are added in a fixed order (no
+//    atomics), so y is bitwise reproducible for a given shape and M.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -41,8 +45,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr uint32_t kOOB = 0x80000000u;  // offset past every stream (< 2 GiB each)
-constexpr int kXChunks = 8;             // x staging: up to 8 dwordx4 per thread
-constexpr int kEntries = 4;             // side-record entries prefetched per thread
 constexpr uint32_t kOneOne = 0x3C003C00u;  // fp16 pair (1.0, 1.0)
 
 __device__ __forceinline__ rsrc_t mk(const void* p, uint32_t bytes) {
@@ -69,15 +71,14 @@ __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
-// fp16 pair (x[a], x[b]) from raw pairs xr[i] = (x[2i], x[2i+1]).
-__device__ __forceinline__ uint32_t pick(const uint32_t* xr, int a, int b) {
-  const uint32_t lo = (xr[a >> 1] >> ((a & 1) * 16)) & 0xffffu;
-  const uint32_t hi = (xr[b >> 1] >> ((b & 1) * 16)) & 0xffffu;
-  return lo | (hi << 16);
+__device__ __forceinline__ uint64_t ld64side(rsrc_t r, uint32_t off) {
+  const u32x2 v = ld64(r, off);
+  return uint64_t(v[0]) | (uint64_t(v[1]) << 32);
 }
 
-// 2-bit fields (hi plane bit, lo plane bit) for the even / odd columns of a
-// 32-column block, aligned with the base-stream dwords 2d / 2d+1.
+// 2-bit fields (hi plane bit, lo plane bit) aligned with the base-stream
+// dwords 2d / 2d+1 from two plane dwords d (bit 2j + e is field j of S0 dword
+// 2d + e).
 __device__ __forceinline__ void pair_fields(uint32_t phi, uint32_t plo, uint32_t& ev, uint32_t& od) {
   ev = bfi(0x55555555u, plo, phi << 1);
   od = bfi(0xAAAAAAAAu, phi, plo >> 1);
@@ -90,18 +91,16 @@ __device__ __forceinline__ void nibbles(uint32_t hw, uint32_t lw, uint32_t& zlo,
 }
 
 struct GemvParams {
-  const uint8_t* s0;       // base stream, chunk 0 (chunk 1 follows at +chunk_bytes)
-  const uint8_t* planes;   // plane 3 (plane k at +(k-3)*chunk_bytes)
+  const uint8_t* s0;       // base stream chunk 0; chunk 1 and planes 3..N follow at a stride of chunk_bytes
   const uint8_t* meta;
   const uint8_t* row_ptr;
   const uint8_t* side;     // side record, one u64 per entry
-  const uint8_t* x;
+  const uint32_t* x;       // fp16 pairs
   float* y;
   uint32_t chunk_bytes, meta_bytes, side_bytes, rp_bytes, x_bytes;
-  int32_t R, C, T, g, rpp, P, NP, RB;
-  int32_t red;             // tiles per row when rows are reduced in the loop (T | 64), else 0
-  int32_t ppitch;          // LDS floats per row of tile partials (T + 1) when red == 0
-  uint32_t lds_rp, lds_meta, lds_part, lds_corr;
+  int32_t R, C, T, S;      // rows, cols, tiles per row, waves (column slices) per workgroup
+  int32_t g;
+  uint32_t lds_sx, lds_part;  // LDS offsets of the group sums and the row partials (x at 0)
 };
 
 template <int M, int GU>
@@ -111,14 +110,17 @@ struct Slot {
   uint32_t meta[GU];                 // (lo | s << 16) of the tile's groups
 };
 
+// Loads of one tile column.  rW covers the base stream and the planes, which
+// follow each other at a stride of chunk bytes (chunk k at soffset k * chunk);
+// an out-of-range voffset reads zeros.
 template <int M, int GU>
-__device__ __forceinline__ void issue(Slot<M, GU>& s, const rsrc_t& rA, const rsrc_t& rB,
-                                      const rsrc_t* rP, const rsrc_t& rMeta, uint32_t tile, bool ok) {
+__device__ __forceinline__ void issue(Slot<M, GU>& s, const rsrc_t& rW, uint32_t chunk,
+                                      const rsrc_t& rMeta, uint32_t tile, bool ok) {
   const uint32_t off = ok ? tile * 16u : kOOB;
-  s.a = ld128(rA, off);
-  s.b = ld128(rB, off);
+  s.a = __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0);
+  s.b = __builtin_amdgcn_raw_buffer_load_b128(rW, off, int(chunk), 0);
 #pragma unroll
-  for (int k = 0; k < M - 2; k++) s.pl[k] = ld128(rP[k], off);
+  for (int k = 0; k < M - 2; k++) s.pl[k] = __builtin_amdgcn_raw_buffer_load_b128(rW, off, int((k + 2) * chunk), 0);
   const uint32_t offm = ok ? tile * (4u * GU) : kOOB;
   if constexpr (GU == 1) {
     s.meta[0] = ld32(rMeta, offm);
@@ -135,387 +137,295 @@ __device__ __forceinline__ uint32_t s0_dword(const u32x4& a, const u32x4& b, int
   return dw < 4 ? a[dw] : b[dw - 4];
 }
 
-// sum over the tile of (s_M u_M + lo_M) x, i.e. Eq. 10 summed per group.
+// Products of one 32-column quarter d of a tile (S0 dwords 2d, 2d+1, plane
+// dwords d) with its x pairs xq[0..15]; accumulators of the quarter.
 template <int M, int GU>
-__device__ __forceinline__ float tile_partial(const Slot<M, GU>& s, const uint32_t* xp, const float* sx) {
-  constexpr float kM = float((1 << (M - 2)) - 1) / float(1 << (M - 1));  // (2^(M-2)-1)/2^(M-1)
-  float sum[GU];
+__device__ __forceinline__ void quarter(const Slot<M, GU>& s, int d, const uint32_t* xq,
+                                        float* acc) {
   if constexpr (M == 2) {
-    float acc[GU][5];
+    // fields j = 0..4 in place (value q 2^(2j) 2^-24), 5..7 after a shift by 6
 #pragma unroll
-    for (int gi = 0; gi < GU; gi++)
-#pragma unroll
-      for (int i = 0; i < 5; i++) acc[gi][i] = 0.f;
-#pragma unroll
-    for (int dw = 0; dw < 8; dw++) {
-      const int gi = (dw >> 1) * GU / 4;
-      const uint32_t w = s0_dword(s.a, s.b, dw);
-      const uint32_t* xq = xp + dw * 8;
-      acc[gi][0] = dot2(w & 0x00030003u, xq[0], acc[gi][0]);
-      acc[gi][1] = dot2(w & 0x000C000Cu, xq[1], acc[gi][1]);
-      acc[gi][2] = dot2(w & 0x00300030u, xq[2], acc[gi][2]);
-      acc[gi][3] = dot2(w & 0x00C000C0u, xq[3], acc[gi][3]);
-      acc[gi][4] = dot2(w & 0x03000300u, xq[4], acc[gi][4]);
+    for (int e = 0; e < 2; e++) {
+      const uint32_t w = s0_dword(s.a, s.b, 2 * d + e);
+      const uint32_t* x8 = xq + 8 * e;
+      acc[0] = dot2(w & 0x00030003u, x8[0], acc[0]);
+      acc[1] = dot2(w & 0x000C000Cu, x8[1], acc[1]);
+      acc[2] = dot2(w & 0x00300030u, x8[2], acc[2]);
+      acc[3] = dot2(w & 0x00C000C0u, x8[3], acc[3]);
+      acc[4] = dot2(w & 0x03000300u, x8[4], acc[4]);
       const uint32_t t = w >> 6;
-      acc[gi][2] = dot2(t & 0x00300030u, xq[5], acc[gi][2]);
-      acc[gi][3] = dot2(t & 0x00C000C0u, xq[6], acc[gi][3]);
-      acc[gi][4] = dot2(t & 0x03000300u, xq[7], acc[gi][4]);
+      acc[2] = dot2(t & 0x00300030u, x8[5], acc[2]);
+      acc[3] = dot2(t & 0x00C000C0u, x8[6], acc[3]);
+      acc[4] = dot2(t & 0x03000300u, x8[7], acc[4]);
+    }
+  } else {
+    uint32_t ye, yo;
+    const uint32_t p3 = s.pl[0][d];
+    if constexpr (M >= 4) {
+      pair_fields(p3, s.pl[1][d], ye, yo);
+    } else {
+      ye = (p3 << 1) & 0xAAAAAAAAu;
+      yo = p3 & 0xAAAAAAAAu;
+    }
+    uint32_t ve = 0, vo = 0, we = 0, wo = 0;
+    if constexpr (M >= 5) {
+      const uint32_t p5 = s.pl[2][d];
+      if constexpr (M >= 6) {
+        pair_fields(p5, s.pl[3][d], ve, vo);
+      } else {
+        ve = (p5 << 1) & 0xAAAAAAAAu;
+        vo = p5 & 0xAAAAAAAAu;
+      }
+      if constexpr (M >= 7) {
+        const uint32_t p7 = s.pl[4][d];
+        if constexpr (M >= 8) {
+          pair_fields(p7, s.pl[5][d], we, wo);
+        } else {
+          we = (p7 << 1) & 0xAAAAAAAAu;
+          wo = p7 & 0xAAAAAAAAu;
+        }
+      }
     }
 #pragma unroll
-    for (int gi = 0; gi < GU; gi++)
-      sum[gi] = acc[gi][0] * 0x1p24f + acc[gi][1] * 0x1p22f + acc[gi][2] * 0x1p20f +
-                acc[gi][3] * 0x1p18f + acc[gi][4] * 0x1p16f;
-  } else {
-    float aA[GU], aB[GU], aC[GU];
+    for (int e = 0; e < 2; e++) {
+      // S0 dword w = 2d + e: nibble m of z[h] (low / high half) is the code of
+      // field 2m + h / 8 + 2m + h, i.e. of x pair 8w + 2m + h.
+      const uint32_t* xw = xq + 8 * e;
+      uint32_t z[2];
+      nibbles(s0_dword(s.a, s.b, 2 * d + e), e ? yo : ye, z[0], z[1]);
 #pragma unroll
-    for (int gi = 0; gi < GU; gi++) { aA[gi] = 0.f; aB[gi] = 0.f; aC[gi] = 0.f; }
-#pragma unroll
-    for (int d = 0; d < 4; d++) {
-      const int gi = d * GU / 4;
-      uint32_t ye, yo;
-      const uint32_t p3 = s.pl[0][d];
-      if constexpr (M >= 4) {
-        pair_fields(p3, s.pl[1][d], ye, yo);
-      } else {
-        ye = (p3 << 1) & 0xAAAAAAAAu;
-        yo = p3 & 0xAAAAAAAAu;
+      for (int h = 0; h < 2; h++) {
+        const uint32_t zz = z[h], t = zz >> 8;
+        acc[0] = dot2(zz & 0x000F000Fu, xw[h], acc[0]);
+        acc[1] = dot2(zz & 0x00F000F0u, xw[2 + h], acc[1]);
+        acc[0] = dot2(t & 0x000F000Fu, xw[4 + h], acc[0]);
+        acc[1] = dot2(t & 0x00F000F0u, xw[6 + h], acc[1]);
       }
-      uint32_t ve = 0, vo = 0, we = 0, wo = 0;
       if constexpr (M >= 5) {
-        const uint32_t p5 = s.pl[2][d];
-        if constexpr (M >= 6) {
-          pair_fields(p5, s.pl[3][d], ve, vo);
-        } else {
-          ve = (p5 << 1) & 0xAAAAAAAAu;
-          vo = p5 & 0xAAAAAAAAu;
-        }
-        if constexpr (M >= 7) {
-          const uint32_t p7 = s.pl[4][d];
-          if constexpr (M >= 8) {
-            pair_fields(p7, s.pl[5][d], we, wo);
-          } else {
-            we = (p7 << 1) & 0xAAAAAAAAu;
-            wo = p7 & 0xAAAAAAAAu;
-          }
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 2; e++) {
-        uint32_t z[2];
-        nibbles(s0_dword(s.a, s.b, 2 * d + e), e ? yo : ye, z[0], z[1]);
+        uint32_t v[2];
+        nibbles(e ? vo : ve, e ? wo : we, v[0], v[1]);
 #pragma unroll
         for (int h = 0; h < 2; h++) {
-          const uint32_t* xq = xp + ((d * 2 + e) * 2 + h) * 4;
-          const uint32_t zz = z[h], t = zz >> 8;
-          aA[gi] = dot2(zz & 0x000F000Fu, xq[0], aA[gi]);
-          aB[gi] = dot2(zz & 0x00F000F0u, xq[1], aB[gi]);
-          aA[gi] = dot2(t & 0x000F000Fu, xq[2], aA[gi]);
-          aB[gi] = dot2(t & 0x00F000F0u, xq[3], aB[gi]);
-        }
-        if constexpr (M >= 5) {
-          uint32_t v[2];
-          nibbles(e ? vo : ve, e ? wo : we, v[0], v[1]);
-#pragma unroll
-          for (int h = 0; h < 2; h++) {
-            const uint32_t* xq = xp + ((d * 2 + e) * 2 + h) * 4;
-            const uint32_t zz = v[h], t = zz >> 8;
-            aB[gi] = dot2(zz & 0x000F000Fu, xq[0], aB[gi]);
-            aC[gi] = dot2(zz & 0x00F000F0u, xq[1], aC[gi]);
-            aB[gi] = dot2(t & 0x000F000Fu, xq[2], aB[gi]);
-            aC[gi] = dot2(t & 0x00F000F0u, xq[3], aC[gi]);
-          }
+          const uint32_t zz = v[h], t = zz >> 8;
+          acc[1] = dot2(zz & 0x000F000Fu, xw[h], acc[1]);
+          acc[2] = dot2(zz & 0x00F000F0u, xw[2 + h], acc[2]);
+          acc[1] = dot2(t & 0x000F000Fu, xw[4 + h], acc[1]);
+          acc[2] = dot2(t & 0x00F000F0u, xw[6 + h], acc[2]);
         }
       }
     }
-    // s_M sum(u_M x) = s * (aA 2^22 + aB 2^18 + aC 2^14) for every M >= 3.
+  }
+}
+
+// sum over one tile of (s_M u_M + lo_M) x, i.e. Eq. 10 summed per group.
+// xl: the tile's 64 x pairs in LDS (wave-uniform address), read one quarter
+// ahead of use; sx: the tile's per-group sum(x).
+template <int M, int GU>
+__device__ __forceinline__ float tile_partial(const Slot<M, GU>& s, const uint32_t* xl, const float* sx) {
+  constexpr float kM = float((1 << (M - 2)) - 1) / float(1 << (M - 1));  // (2^(M-2)-1)/2^(M-1)
+  constexpr int kAcc = M == 2 ? 5 : 3;
+  float acc[GU][kAcc];
 #pragma unroll
-    for (int gi = 0; gi < GU; gi++)
-      sum[gi] = aA[gi] * 0x1p22f + aB[gi] * 0x1p18f + (M >= 5 ? aC[gi] * 0x1p14f : 0.f);
+  for (int gi = 0; gi < GU; gi++)
+#pragma unroll
+    for (int i = 0; i < kAcc; i++) acc[gi][i] = 0.f;
+  const u32x4* xl4 = reinterpret_cast<const u32x4*>(xl);
+  uint32_t xq[2][16];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const u32x4 v = xl4[k];
+    xq[0][4 * k] = v[0]; xq[0][4 * k + 1] = v[1]; xq[0][4 * k + 2] = v[2]; xq[0][4 * k + 3] = v[3];
+  }
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    if (d < 3) {
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const u32x4 v = xl4[4 * (d + 1) + k];
+        uint32_t* o = xq[(d + 1) & 1];
+        o[4 * k] = v[0]; o[4 * k + 1] = v[1]; o[4 * k + 2] = v[2]; o[4 * k + 3] = v[3];
+      }
+    }
+    float* a = acc[d * GU / 4];
+    quarter<M, GU>(s, d, xq[d & 1], a);
+    // An empty volatile statement that takes the quarter's accumulators and
+    // clobbers memory: the quarter is computed here, and the reads of quarter
+    // d + 2 cannot move above it, so at most two quarters of x are live.
+    if constexpr (kAcc == 5)
+      asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]) :: "memory");
+    else
+      asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]) :: "memory");
   }
   float part = 0.f;
 #pragma unroll
   for (int gi = 0; gi < GU; gi++) {
+    float q;
+    if constexpr (M == 2)   // s_2 sum(q x): field j accumulated at scale 2^(2j-24)
+      q = acc[gi][0] * 0x1p24f + acc[gi][1] * 0x1p22f + acc[gi][2] * 0x1p20f + acc[gi][3] * 0x1p18f +
+          acc[gi][4] * 0x1p16f;
+    else                    // s_M sum(u_M x) = s * (A 2^22 + B 2^18 + C 2^14) for every M >= 3
+      q = acc[gi][0] * 0x1p22f + acc[gi][1] * 0x1p18f + (M >= 5 ? acc[gi][2] * 0x1p14f : 0.f);
     const float lo = h2f(s.meta[gi] & 0xffffu), st = h2f(s.meta[gi] >> 16);
-    part += st * (sum[gi] - kM * sx[gi]) + lo * sx[gi];
+    part += st * (q - kM * sx[gi]) + lo * sx[gi];
   }
   return part;
 }
 
-// One step of a segmented inclusive scan inside 16-lane rows (DPP row_shr):
-// add the value SH lanes down when it belongs to the same segment r.
+// Add the value SH lanes down inside a 16-lane DPP row (0 where there is none).
 template <int SH>
-__device__ __forceinline__ float seg_step(float v, int r) {
-  const int pv = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + SH, 0xf, 0xf, true);
-  const int pr = __builtin_amdgcn_update_dpp(-1, r, 0x110 + SH, 0xf, 0xf, false);
-  return pr == r ? v + __builtin_bit_cast(float, pv) : v;
-}
-// Carry across 16-lane rows: row_bcast:15 hands lane 15 of row 0/2 to rows
-// 1/3 (row mask 0xa); row_bcast:31 hands lane 31 to rows 2 and 3 (mask 0xc).
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ float seg_bcast(float v, int r) {
-  const int pv = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xf, false);
-  const int pr = __builtin_amdgcn_update_dpp(-1, r, CTRL, ROWMASK, 0xf, false);
-  return pr == r ? v + __builtin_bit_cast(float, pv) : v;
-}
-// Segmented inclusive scan over the 64 lanes of a wave (segment ids sorted by
-// lane): afterwards the last lane of every segment holds the segment's sum.
-__device__ __forceinline__ float seg_scan64(float v, int r) {
-  v = seg_step<1>(v, r);
-  v = seg_step<2>(v, r);
-  v = seg_step<4>(v, r);
-  v = seg_step<8>(v, r);
-  v = seg_bcast<0x142, 0xa>(v, r);
-  v = seg_bcast<0x143, 0xc>(v, r);
-  return v;
+__device__ __forceinline__ float row_shr_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                   0x110 + SH, 0xf, 0xf, true));
 }
 
-// LDS column index of x: every 128-column tile is followed by 16 bytes of
-// padding (conflict-free row reads in the correction phase).
-__device__ __forceinline__ int xcol(int c) { return c + ((c >> 7) << 3); }
-
-__device__ __forceinline__ uint64_t ld64side(rsrc_t r, uint32_t off) {
-  const u32x2 v = ld64(r, off);
-  return uint64_t(v[0]) | (uint64_t(v[1]) << 32);
-}
+constexpr int kEntries = 2;    // side-record entries prefetched per lane
+constexpr int kXChunks = 4;    // 16-byte x chunks staged per lane: up to 4 steps per wave
+constexpr int kXPitch = 68;    // LDS dwords per tile of x: 64 + 4 of padding
 
 template <int M, int GU, int D>
-__global__ void __launch_bounds__(512) gemv_kernel(const GemvParams p) {
+__global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
-  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);
-  int32_t* rp_s = reinterpret_cast<int32_t*>(lds + p.lds_rp);
-  uint32_t* meta_s = reinterpret_cast<uint32_t*>(lds + p.lds_meta);
-  float* part_s = reinterpret_cast<float*>(lds + p.lds_part);
-  float* corr_s = reinterpret_cast<float*>(lds + p.lds_corr);
+  uint32_t* xs = reinterpret_cast<uint32_t*>(lds);            // x pairs, tile t at t * kXPitch
+  float* sx_s = reinterpret_cast<float*>(lds + p.lds_sx);     // sum(x) per group
+  float* part_s = reinterpret_cast<float*>(lds + p.lds_part); // lane partials per wave
 
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  const int r0 = blockIdx.x * p.RB;
-  const int rip = tid / p.T;            // row slot within a pass
-  const int t = tid - rip * p.T;        // tile column
-  const bool act = rip < p.rpp;
-  const int rows_here = min(p.RB, p.R - r0);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int blk = blockIdx.x;
+  const int cg = lane >> 4;                       // tile column within the four
+  const int r = blk * 16 + (lane & 15);
+  const int Q = (p.T + 3) >> 2;                    // groups of four tile columns
+  const int q0 = (w * Q) / p.S, nq = ((w + 1) * Q) / p.S - q0;
+  const uint32_t ubase = uint32_t(blk * p.T + 4 * q0) * 16u + uint32_t(lane);  // tile of step 0
 
-  const rsrc_t rA = mk(p.s0, p.chunk_bytes);
-  const rsrc_t rB = mk(p.s0 + p.chunk_bytes, p.chunk_bytes);
-  rsrc_t rP[M > 2 ? M - 2 : 1];
-#pragma unroll
-  for (int k = 0; k < M - 2; k++) rP[k] = mk(p.planes + uint64_t(k) * p.chunk_bytes, p.chunk_bytes);
+  const uint32_t chunk = p.chunk_bytes;
+  const rsrc_t rW = mk(p.s0, uint32_t(M) * chunk);
   const rsrc_t rMeta = mk(p.meta, p.meta_bytes);
   const rsrc_t rX = mk(p.x, p.x_bytes);
   const rsrc_t rRp = mk(p.row_ptr, p.rp_bytes);
   const rsrc_t rSide = mk(p.side, p.side_bytes);
+  auto valid = [&](int i) { return i < nq && 4 * (q0 + i) + cg < p.T; };
 
-  // --- prologue.  Load order = arrival order: the workgroup's side-record
-  //     range, this lane's x slice, x chunks and row_ptr for the LDS copies used
-  //     at the end, then every pass of weights.  No barrier stands between the
-  //     loads and the first pass.
-  const uint32_t e0u = ld32(rRp, uint32_t(r0) * 4u);
-  const uint32_t e1u = ld32(rRp, uint32_t(r0 + rows_here) * 4u);
-  u32x4 xq[16];
-  const uint32_t xbase = uint32_t(act ? t : 0) * 256u;
-#pragma unroll
-  for (int k = 0; k < 16; k++) xq[k] = ld128(rX, xbase + 16u * k);
-  const int xchunks = p.C >> 3;
+  // --- prologue, in arrival order: the row's side-record range, the x of this
+  //     wave's tile columns, then D steps of weights.  Nothing waits on
+  //     row_ptr before the first step.
+  const bool row_ok = r < p.R;
+  const uint32_t e0u = ld32(rRp, row_ok ? uint32_t(r) * 4u : kOOB);
+  const uint32_t e1u = ld32(rRp, row_ok ? uint32_t(r + 1) * 4u : kOOB);
+  const int cbase = 4 * q0 * 16;                         // first x chunk (8 columns) of the wave
+  const int nch = min(4 * nq * 16, (p.C >> 3) - cbase);  // x chunks of the wave
   u32x4 xv[kXChunks];
 #pragma unroll
-  for (int i = 0; i < kXChunks; i++) {
-    const int ci = tid + i * nthr;
-    xv[i] = ld128(rX, ci < xchunks ? uint32_t(ci) * 16u : kOOB);
-  }
-  uint32_t rpv[2];                       // row_ptr[r0 + j], j = tid, tid + nthr (<= rows_here)
-#pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int j = tid + i * nthr;
-    rpv[i] = ld32(rRp, j <= rows_here ? uint32_t(r0 + j) * 4u : kOOB);
+  for (int k = 0; k < kXChunks; k++) {
+    const int c = lane + 64 * k;
+    xv[k] = ld128(rX, c < nch ? uint32_t(cbase + c) * 16u : kOOB);
   }
   __builtin_amdgcn_sched_barrier(0);
   Slot<M, GU> sl[D];
 #pragma unroll
-  for (int i = 0; i < D; i++) {          // slot by slot: pass i's loads complete first
-    const int row = r0 + i * p.rpp + rip;
-    issue(sl[i], rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && i < p.NP && row < p.R);
+  for (int i = 0; i < D; i++) {
+    issue(sl[i], rW, chunk, rMeta, ubase + uint32_t(i) * 64u, valid(i));
     __builtin_amdgcn_sched_barrier(0);
   }
-  // LDS copies of x and row_ptr for the end (read after the loop's barrier).
-  // The writes are unconditional (spare ones land in pad slots) so the loads
-  // above are never sunk into a branch and waited on late.
-#pragma unroll
-  for (int i = 0; i < kXChunks; i++) {
-    const int ci = tid + i * nthr;
-    *reinterpret_cast<u32x4*>(xs + (ci < xchunks ? xcol(ci * 8) : xcol(p.C))) = xv[i];
-  }
-#pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int j = tid + i * nthr;
-    rp_s[j <= rows_here ? j : p.RB + 1] = int32_t(rpv[i]);
-  }
-  const int e0 = int(e0u), e1 = int(e1u);
 
-  // --- x slice of this lane's tile as permuted fp16 pairs; per-group sum(x).
-  uint32_t xp[64];
-  float sx[GU];
+  // --- this wave's x into LDS, and sum(x) per group: a chunk holds 8
+  //     columns, a group 16 / GU consecutive chunks = lanes of one DPP row,
+  //     summed with row_shr steps.  Spare lanes write to spare slots so no load
+  //     is sunk into a branch.  Only this wave reads these before the barrier.
+  constexpr int kCpg = 16 / GU;
+  const int li = lane & (kCpg - 1);
 #pragma unroll
-  for (int gi = 0; gi < GU; gi++) sx[gi] = 0.f;
+  for (int k = 0; k < kXChunks; k++) {
+    const int c = lane + 64 * k;
+    const bool ok = c < nch;
+    const int ci = cbase + c;
+    const int xo = ok ? (ci >> 4) * kXPitch + (ci & 15) * 4 : p.T * kXPitch;
+    *reinterpret_cast<u32x4*>(xs + xo) = xv[k];
+    float v = 0.f;
 #pragma unroll
-  for (int d = 0; d < 4; d++) {
-    uint32_t xr[64];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; q4++) {
-      const u32x4 v = xq[4 * d + q4];
-      xr[16 * d + 4 * q4 + 0] = v[0]; xr[16 * d + 4 * q4 + 1] = v[1];
-      xr[16 * d + 4 * q4 + 2] = v[2]; xr[16 * d + 4 * q4 + 3] = v[3];
-    }
-    const int gi = d * GU / 4;
-#pragma unroll
-    for (int i = 0; i < 16; i++) sx[gi] = dot2(xr[16 * d + i], kOneOne, sx[gi]);
-    if constexpr (M == 2) {
-#pragma unroll
-      for (int e = 0; e < 2; e++)
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-          xp[(2 * d + e) * 8 + i] = pick(xr, 32 * d + 2 * i + e, 32 * d + 16 + 2 * i + e);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 2; e++)
-#pragma unroll
-        for (int h = 0; h < 2; h++)
-#pragma unroll
-          for (int m = 0; m < 4; m++)
-            xp[((d * 2 + e) * 2 + h) * 4 + m] =
-                pick(xr, 32 * d + 4 * m + 2 * h + e, 32 * d + 16 + 4 * m + 2 * h + e);
-    }
+    for (int i = 0; i < 4; i++) v = dot2(xv[k][i], kOneOne, v);
+    float u;
+    u = row_shr_add<1>(v); v = li >= 1 ? u : v;
+    u = row_shr_add<2>(v); v = li >= 2 ? u : v;
+    if constexpr (kCpg >= 8) { u = row_shr_add<4>(v); v = li >= 4 ? u : v; }
+    if constexpr (kCpg >= 16) { u = row_shr_add<8>(v); v = li >= 8 ? u : v; }
+    sx_s[ok && li == kCpg - 1 ? ci / kCpg : p.C / p.g] = v;
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // --- main loop.  A pass: the lane's tile partial; when a row's tiles are a
-  //     power-of-two group of lanes inside one wave the row is summed at once
-  //     with DPP and one value per row goes to LDS, otherwise one value per
-  //     tile.  The slot is then reloaded with pass + D (out of range -> zeros,
-  //     no traffic), which keeps every wait count path-independent.
-  const int lane = tid & 63;
+  // --- main loop; the slot of step i is reloaded with step i + D (out of
+  //     range -> zeros, no traffic), which keeps every wait count
+  //     path-independent.  After the first step (row_ptr long in) the lane's
+  //     first side-record entries are requested: entries e0 + j with
+  //     j = 4 w + cg modulo 4 S, applied after the loop.
+  const int stride = 4 * p.S;
+  int e0 = 0, e1 = 0;
   uint64_t ent[kEntries];
-  auto step_pass = [&](Slot<M, GU>& sl_i, int pass) {
-    if (pass < p.NP) {
-      float part = tile_partial<M, GU>(sl_i, xp, sx);
-      if (p.red > 0) {
-        // Every DPP step runs on all lanes (a lane reading a masked-off
-        // neighbour would see 0); groups narrower than a 16-lane row then
-        // keep the sum only where the source lane is in their own group.
-        const int T = p.red;
-        const int li = lane & (T - 1);
-        float v;
-        if (T >= 2) { v = seg_step<1>(part, 0); part = li >= 1 ? v : part; }
-        if (T >= 4) { v = seg_step<2>(part, 0); part = li >= 2 ? v : part; }
-        if (T >= 8) { v = seg_step<4>(part, 0); part = li >= 4 ? v : part; }
-        if (T >= 16) part = seg_step<8>(part, 0);
-        if (T >= 32) part = seg_bcast<0x142, 0xa>(part, T == 32 ? (lane >> 5) : 0);
-        if (T >= 64) part = seg_bcast<0x143, 0xc>(part, 0);
-        if (li == T - 1 && act) part_s[pass * p.rpp + rip] = part;
-      } else if (act) {
-        part_s[(pass * p.rpp + rip) * p.ppitch + t] = part;
-      }
-      if (act) {
-        const int slot = pass * p.P + tid;
+  float part = 0.f;
+  auto step = [&](Slot<M, GU>& s, int i) {
+    if (i < nq) {
+      const int t = min(4 * (q0 + i) + cg, p.T - 1);   // lanes past the row's end read zeros
+      float sx[GU];
 #pragma unroll
-        for (int gi = 0; gi < GU; gi++) meta_s[slot * GU + gi] = sl_i.meta[gi];
-      }
+      for (int gi = 0; gi < GU; gi++) sx[gi] = sx_s[t * GU + gi];
+      part += tile_partial<M, GU>(s, xs + t * kXPitch, sx);
     }
-    const int np = pass + D;
-    const int row = r0 + np * p.rpp + rip;
-    issue(sl_i, rA, rB, rP, rMeta, uint32_t(row) * p.T + t, act && np < p.NP && row < p.R);
-  };
-  // The first D passes in straight-line code; after the first, fetch this
-  // workgroup's first side-record entries (one u64 each) for the end.
-#pragma unroll
-  for (int i = 0; i < D; i++) {
-    step_pass(sl[i], i);
+    __builtin_amdgcn_sched_barrier(0);   // reuse the slot's registers: no loads hoisted above
+    issue(s, rW, chunk, rMeta, ubase + uint32_t(i + D) * 64u, valid(i + D));
     if (i == 0) {
+      e0 = int(e0u) + 4 * w + cg;
+      e1 = int(e1u);
 #pragma unroll
       for (int j = 0; j < kEntries; j++) {
-        const int e = e0 + tid + j * nthr;
+        const int e = e0 + j * stride;
         ent[j] = ld64side(rSide, e < e1 ? uint32_t(e) * 8u : kOOB);
       }
     }
-  }
-  for (int pb = D; pb < p.NP; pb += D) {
+  };
 #pragma unroll
-    for (int i = 0; i < D; i++) step_pass(sl[i], pb + i);
+  for (int i = 0; i < D; i++) step(sl[i], i);
+  for (int ib = D; ib < nq; ib += D) {
+#pragma unroll
+    for (int i = 0; i < D; i++) step(sl[i], ib + i);
   }
+  __syncthreads();                       // x complete in LDS
+
+  // --- this lane's side-record corrections (a - s 2^(1-M)) x_c, in entry order.
+  constexpr float kHalfUlp = 2.0f / float(1 << M);   // 2^(1-M)
+  const uint16_t* xh = reinterpret_cast<const uint16_t*>(xs);
+  auto corr = [&](uint64_t ev) -> float {
+    const float a = __builtin_bit_cast(float, uint32_t(ev));
+    const float st = h2f(uint32_t(ev >> 32) & 0xffffu);
+    const int c = int(ev >> 48);
+    return (a - st * kHalfUlp) * h2f(xh[(c >> 7) * (2 * kXPitch) + (c & 127)]);
+  };
+#pragma unroll
+  for (int j = 0; j < kEntries; j++)
+    if (e0 + j * stride < e1) part += corr(ent[j]);
+  for (int e = e0 + kEntries * stride; e < e1; e += stride) part += corr(ld64side(rSide, uint32_t(e) * 8u));
+
+  // --- row sums: lane partials in (wave, tile column) order.
+  part_s[w * 64 + lane] = part;
   __syncthreads();
-
-  // --- side-record corrections (P - W_main) x_c, W_main = lo + s (q - 1/2 + 2^(1-M)),
-  //     in chunks of kEntries * nthr entries in entry order.  Within each block
-  //     of 64 consecutive entries (one wave) a segmented scan by row leaves, at
-  //     the last entry of every row run, that run's sum; a row then adds one
-  //     value per 64-entry block it touches.  Fixed order throughout.
-  constexpr float kHeld = -0.5f + 1.0f / float(1 << (M - 1));
-  const int chunk = kEntries * nthr;
-  auto row_of = [&](uint64_t ev) -> int {   // row within the workgroup
-    return int((uint32_t(ev >> 48) - uint32_t(r0)) & 0xffffu);
-  };
-  auto correction = [&](uint64_t ev) -> float {
-    const int c = min(int(uint32_t(ev) & 0x3fffffffu), p.C - 1);
-    const int q = int(uint32_t(ev) >> 30);
-    const int rloc = min(row_of(ev), p.RB - 1);
-    const int slot = (rloc / p.rpp) * p.P + (rloc % p.rpp) * p.T + (c >> 7);
-    const int gi = (c & 127) / p.g;
-    const uint32_t mw = meta_s[slot * GU + gi];
-    const float lo = h2f(mw & 0xffffu), st = h2f(mw >> 16);
-    const float wmain = lo + st * (float(q) + kHeld);
-    return (h2f(uint32_t(ev >> 32) & 0xffffu) - wmain) * h2f(xs[xcol(c)]);
-  };
-  float rowc[2] = {0.f, 0.f};             // this thread's rows: tid and tid + nthr
-  for (int ce = e0; ce < e1; ce += chunk) {
-    if (ce > e0) {                        // rare: more entries than one prefetched chunk
-      __syncthreads();                    // previous chunk consumed
+  if (w == 0 && lane < 16 && row_ok) {
+    float acc = 0.f;
+    for (int k = 0; k < p.S; k++)
 #pragma unroll
-      for (int j = 0; j < kEntries; j++) {
-        const int e = ce + tid + j * nthr;
-        ent[j] = ld64side(rSide, e < e1 ? uint32_t(e) * 8u : kOOB);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kEntries; j++) {
-      const bool ok = ce + tid + j * nthr < e1;
-      corr_s[tid + j * nthr] = seg_scan64(correction(ent[j]), ok ? row_of(ent[j]) : p.RB);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-      const int i = tid + k * nthr;
-      if (i < rows_here) {
-        const int a = max(rp_s[i], ce) - ce, b = min(rp_s[i + 1], ce + chunk) - ce;
-        for (int q = a; q < b; q = (q | 63) + 1) rowc[k] += corr_s[min(b, (q | 63) + 1) - 1];
-      }
-    }
-  }
-
-  // --- row sums: one thread per row.
-#pragma unroll
-  for (int k = 0; k < 2; k++) {
-    const int i = tid + k * nthr;
-    if (i < rows_here) {
-      float acc;
-      if (p.red > 0) {
-        acc = part_s[i];
-      } else {
-        const float* pr = part_s + i * p.ppitch;
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-        int tt = 0;
-        for (; tt + 4 <= p.T; tt += 4) { a0 += pr[tt]; a1 += pr[tt + 1]; a2 += pr[tt + 2]; a3 += pr[tt + 3]; }
-        for (; tt < p.T; tt++) a0 += pr[tt];
-        acc = (a0 + a1) + (a2 + a3);
-      }
-      p.y[r0 + i] = acc + rowc[k];
-    }
+      for (int c = 0; c < 4; c++) acc += part_s[k * 64 + c * 16 + lane];
+    p.y[r] = acc;
   }
 }
 
-// Code dump: one thread per tile writes the 128 codes u_M of its tile.
+// Code dump: one thread per (padded) tile writes the 128 codes u_M (Eq. 8) of
+// its tile, read field by field from the base stream and planes 3..M.
 struct CodesParams {
   const uint8_t* s0;
   const uint8_t* planes;
   uint8_t* codes;
   uint32_t chunk_bytes;
-  int32_t T, C;
+  int32_t R, T, C;
   int64_t tiles;
 };
 
@@ -523,72 +433,30 @@ template <int M>
 __global__ void __launch_bounds__(256) codes_kernel(const CodesParams p) {
   const int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (u >= p.tiles) return;
+  const int64_t row = (u / (16 * int64_t(p.T))) * 16 + (u & 15);
+  const int64_t tc = (u >> 4) % p.T;
+  if (row >= p.R) return;
   const rsrc_t rA = mk(p.s0, p.chunk_bytes), rB = mk(p.s0 + p.chunk_bytes, p.chunk_bytes);
   const uint32_t off = uint32_t(u) * 16u;
   const u32x4 a = ld128(rA, off), b = ld128(rB, off);
   u32x4 pl[M > 2 ? M - 2 : 1];
 #pragma unroll
   for (int k = 0; k < M - 2; k++) pl[k] = ld128(mk(p.planes + uint64_t(k) * p.chunk_bytes, p.chunk_bytes), off);
-  uint32_t out[32];  // out[8d + m] = codes of columns 32d + 4m .. 32d + 4m + 3
-#pragma unroll
-  for (int d = 0; d < 4; d++) {
-    if constexpr (M == 2) {
-#pragma unroll
-      for (int m = 0; m < 8; m++) {
-        uint32_t o = 0;
-#pragma unroll
-        for (int bb = 0; bb < 4; bb++) {
-          const uint32_t w = s0_dword(a, b, 2 * d + (bb & 1));
-          o |= ((w >> (2 * (2 * m + (bb >> 1)))) & 3u) << (8 * bb);
-        }
-        out[8 * d + m] = o;
-      }
-    } else {
-      uint32_t ye, yo;
-      if constexpr (M >= 4) {
-        pair_fields(pl[0][d], pl[1][d], ye, yo);
-      } else {
-        ye = (pl[0][d] << 1) & 0xAAAAAAAAu;
-        yo = pl[0][d] & 0xAAAAAAAAu;
-      }
-      uint32_t ve = 0, vo = 0, we = 0, wo = 0;
-      if constexpr (M >= 5) {
-        if constexpr (M >= 6) pair_fields(pl[2][d], pl[3][d], ve, vo);
-        else { ve = (pl[2][d] << 1) & 0xAAAAAAAAu; vo = pl[2][d] & 0xAAAAAAAAu; }
-        if constexpr (M >= 7) {
-          if constexpr (M >= 8) pair_fields(pl[4][d], pl[5][d], we, wo);
-          else { we = (pl[4][d] << 1) & 0xAAAAAAAAu; wo = pl[4][d] & 0xAAAAAAAAu; }
-        }
-      }
-      uint32_t z[2][2], v[2][2];
-#pragma unroll
-      for (int e = 0; e < 2; e++) {
-        nibbles(s0_dword(a, b, 2 * d + e), e ? yo : ye, z[e][0], z[e][1]);
-        nibbles(e ? vo : ve, e ? wo : we, v[e][0], v[e][1]);
-      }
-#pragma unroll
-      for (int m = 0; m < 8; m++) {
-        uint32_t o = 0;
-#pragma unroll
-        for (int bb = 0; bb < 4; bb++) {
-          const int e = bb & 1, h = bb >> 1;
-          const uint32_t n0 = (z[e][h] >> (4 * m)) & 15u;   // q b3 b4 (zeros below a short read)
-          uint32_t code;
-          if constexpr (M == 3) code = n0 >> 1;
-          else if constexpr (M == 4) code = n0;
-          else code = (n0 << (M - 4)) | (((v[e][h] >> (4 * m)) & 15u) >> (8 - M));
-          o |= code << (8 * bb);
-        }
-        out[8 * d + m] = o;
-      }
-    }
-  }
-  const int64_t row = u / p.T, tc = u % p.T;
   u32x4* dst = reinterpret_cast<u32x4*>(p.codes + row * p.C + tc * 128);
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
+  for (int i = 0; i < 8; i++) {          // columns 16i .. 16i + 15 (S0 dword i)
+    const uint32_t wq = s0_dword(a, b, i);
+    uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int cc = 0; cc < 16; cc++) {
+      const int j = (cc >> 1) + 8 * (cc & 1);            // field of column 16i + cc
+      uint32_t code = (wq >> (2 * j)) & 3u;
+#pragma unroll
+      for (int k = 0; k < M - 2; k++) code = (code << 1) | ((pl[k][i >> 1] >> (2 * j + (i & 1))) & 1u);
+      o[cc >> 2] |= code << (8 * (cc & 3));
+    }
     u32x4 v;
-    v[0] = out[4 * i]; v[1] = out[4 * i + 1]; v[2] = out[4 * i + 2]; v[3] = out[4 * i + 3];
+    v[0] = o[0]; v[1] = o[1]; v[2] = o[2]; v[3] = o[3];
     dst[i] = v;
   }
 }
@@ -597,7 +465,7 @@ __global__ void __launch_bounds__(256) codes_kernel(const CodesParams p) {
 
 // ------------------------------------------------------------- dispatch ----
 struct LaunchCfg {
-  int waves, rpp, NP, RB, grid, L;
+  int S, grid, nt_max;
   size_t lds;
   dev::GemvParams prm;
 };
@@ -613,101 +481,69 @@ static int device_cus() {
   return cus;
 }
 
+static size_t device_lds_limit() {
+  static int lim = 0;
+  if (!lim) {
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess ||
+        hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, d) != hipSuccess || lim <= 0)
+      lim = 64 * 1024;
+  }
+  return size_t(lim);
+}
+
 static int env_int(const char* name, int dflt) {
   const char* e = getenv(name);
   return e ? atoi(e) : dflt;
 }
 
-constexpr size_t kLdsBudget = 64 * 1024;
-// Passes of loads in flight per precision (bounded by the VGPRs of a slot:
-// 8 + 4 (M - 2) + pairs dwords).
-constexpr int kDepth[9] = {0, 0, 8, 4, 4, 2, 2, 2, 2};
-constexpr int kMaxWaves = 8;  // matches __launch_bounds__(512) of the GEMV kernel
+// Tile columns of loads in flight per wave, per precision (bounded by the
+// VGPRs of a slot: 8 + 4 (M - 2) + pairs dwords).
+constexpr int kDepth[9] = {0, 0, 4, 4, 3, 3, 2, 2, 2};
+constexpr int kMaxWaves = 16;   // matches __launch_bounds__(1024) of the GEMV kernel
 
-// LDS carve-up of one workgroup: padded x (plus one spare 16-byte slot),
-// row_ptr of its rows (plus a spare slot), group pairs of every tile it owns,
-// row (or tile) partials, and one chunk of scanned side-record corrections.
-static size_t lds_layout(int C, int GU, int nthr, int NP, int rpp, int P, int T, bool red,
-                         dev::GemvParams* prm) {
-  const size_t units = size_t(NP) * P;
-  const int RB = NP * rpp;
-  size_t o = size_t(C) * 2 + size_t(C / kTileCols) * 16 + 16;
-  if (prm) prm->lds_rp = uint32_t(o);
-  o += size_t(RB + 2) * 4;
+// LDS carve-up: x padded to 68 dwords per tile (plus a spare chunk), sum(x)
+// per group (plus a spare slot), per-wave lane partials.
+static size_t lds_layout(int C, int g, int S, dev::GemvParams* prm) {
+  size_t o = size_t(C / kTileCols + 1) * dev::kXPitch * 4;
+  if (prm) prm->lds_sx = uint32_t(o);
+  o += (size_t(C / g) + 1) * 4;
   o = (o + 15) & ~size_t(15);
-  if (prm) prm->lds_meta = uint32_t(o);
-  o += units * 4 * GU;
   if (prm) prm->lds_part = uint32_t(o);
-  o += red ? size_t(RB) * 4 : size_t(RB) * (T + 1) * 4;
-  o = (o + 15) & ~size_t(15);
-  if (prm) prm->lds_corr = uint32_t(o);
-  o += size_t(dev::kEntries) * nthr * 4;
+  o += size_t(S) * 64 * 4;
   return o;
 }
 
-// Rows are summed inside the loop when a row's tiles form a power-of-two group
-// of lanes within one wave.
-static bool row_reduce(int T) { return T <= 64 && (T & (T - 1)) == 0; }
-
-// Launch shape for one GEMV: k waves per workgroup, rpp rows side by side
-// (rpp * tiles_per_row lanes busy), NP passes per workgroup.  Among the shapes
-// that fit LDS, pick the lowest estimated cost on the busiest CU: rounds of
-// workgroups x (passes + 2 of overhead) x lanes, a third more when not all
-// passes fit in flight (NP > depth); ties go to more waves.  STAGQ_WAVES / STAGQ_NP
-// override the choice (tuning).
-static bool plan_gemv(const ImageHeader& h, int GU, int depth, LaunchCfg* c) {
+// Launch shape: one workgroup per 16-row block, S waves splitting the row's
+// groups of four tile columns.  S is the smallest count that puts about two
+// waves on every SIMD (8 per CU), within [ceil(groups / 4), min(16, groups)]
+// (a wave stages the x of at most 4 steps).  STAGQ_WAVES overrides the choice
+// (tuning).
+static bool plan_gemv(const ImageHeader& h, LaunchCfg* c) {
   const int T = h.cols / kTileCols;
-  const int R = h.rows;
-  const int cus = device_cus();
-  const int kmin = std::max(std::max((T + 63) / 64, 1),
-                            (h.cols / 8 + dev::kXChunks * 64 - 1) / (dev::kXChunks * 64));
-  const int k_env = env_int("STAGQ_WAVES", 0), np_env = env_int("STAGQ_NP", 0);
-  bool found = false;
-  long best_work = 0;
-  int best_k = 0, best_np = 0;
-  bool best_fly = false;
-  for (int k = kmin; k <= kMaxWaves; k++) {
-    if (k_env && k != k_env) continue;
-    const int nthr = 64 * k, rpp = nthr / T;
-    if (rpp < 1) continue;
-    const double util = double(rpp * T) / nthr;
-    if (util < 0.85 && !k_env) continue;
-    const int passes = (R + rpp - 1) / rpp;
-    for (int np = 1; np <= passes; np++) {
-      if (np_env && np != np_env) continue;
-      if (lds_layout(h.cols, GU, nthr, np, rpp, rpp * T, T, row_reduce(T), nullptr) > kLdsBudget ||
-          np * rpp + 1 > 2 * nthr)
-        break;
-      const int grid = (passes + np - 1) / np;
-      const bool fly = np <= depth;
-      // lane-passes on the busiest CU, each workgroup paying about two passes
-      // of prologue and epilogue; a third more when passes must wait for slots
-      const long work = long((grid + cus - 1) / cus) * (np + 2) * nthr * (fly ? 3 : 4);
-      const bool better = !found || work < best_work ||
-                          (work == best_work && fly && !best_fly) ||
-                          (work == best_work && fly == best_fly && k > best_k);
-      if (better) { found = true; best_work = work; best_k = k; best_np = np; best_fly = fly; }
-    }
-  }
-  if (!found) return false;
-  const int k = best_k, NP = best_np;
-  const int nthr = 64 * k, rpp = nthr / T, P = rpp * T;
-  const int RB = NP * rpp;
-  c->waves = k; c->rpp = rpp; c->NP = NP; c->RB = RB;
-  c->grid = (R + RB - 1) / RB;
-  c->L = 0;
-  const bool red = row_reduce(T);
-  c->lds = lds_layout(h.cols, GU, nthr, NP, rpp, P, T, red, &c->prm);
-  c->prm.R = R; c->prm.C = h.cols; c->prm.T = T; c->prm.g = h.group; c->prm.rpp = rpp;
-  c->prm.P = P; c->prm.NP = NP; c->prm.RB = RB;
-  c->prm.red = red ? T : 0;
-  c->prm.ppitch = T + 1;
+  const int Q = (T + 3) / 4;
+  const int nblk = h.blocks;
+  const int smin = (Q + dev::kXChunks - 1) / dev::kXChunks;
+  const int smax = std::min(kMaxWaves, Q);
+  if (nblk <= 0 || smin > smax) return false;
+  const int target = 2 * 4 * device_cus();
+  int S = (target + nblk - 1) / nblk;
+  S = std::max(smin, std::min(smax, S));
+  const int s_env = env_int("STAGQ_WAVES", 0);
+  if (s_env) S = s_env;
+  if (S < smin || S > smax) return false;
+  c->S = S;
+  c->grid = nblk;
+  c->nt_max = (Q + S - 1) / S;
+  c->lds = lds_layout(h.cols, h.group, S, &c->prm);
+  if (c->lds > device_lds_limit()) return false;
+  c->prm.R = h.rows; c->prm.C = h.cols; c->prm.T = T; c->prm.S = S; c->prm.g = h.group;
   return true;
 }
 
 template <int M, int GU, int D>
 static hipError_t launch_gemv(const LaunchCfg& c, hipStream_t st) {
-  hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D>), dim3(c.grid), dim3(64 * c.waves), c.lds, st, c.prm);
+  hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D>), dim3(c.grid), dim3(64 * c.S), c.lds, st, c.prm);
   return hipGetLastError();
 }
 
@@ -796,19 +632,18 @@ int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stre
   if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 4) return STAGQ_EALIGN;
   const int GU = kTileCols / H.group;
   LaunchCfg c;
-  if (!plan_gemv(H, GU, kDepth[bits], &c)) return STAGQ_ESHAPE;
+  if (!plan_gemv(H, &c)) return STAGQ_ESHAPE;
   const uint8_t* b = h->dev;
   c.prm.s0 = b + H.off_s0;
-  c.prm.planes = b + H.off_planes;
   c.prm.meta = b + H.off_meta;
   c.prm.row_ptr = b + H.off_rowptr;
   c.prm.side = b + H.off_side;
-  c.prm.x = static_cast<const uint8_t*>(x);
+  c.prm.x = static_cast<const uint32_t*>(x);
   c.prm.y = y;
   c.prm.chunk_bytes = uint32_t(H.bytes_s0_chunk);
   c.prm.meta_bytes = uint32_t(H.bytes_meta);
   c.prm.side_bytes = uint32_t(H.nnz * 8);
-  c.prm.rp_bytes = uint32_t((H.rows + 1) * 4);
+  c.prm.rp_bytes = uint32_t((int64_t(H.rows) + 1) * 4);
   c.prm.x_bytes = uint32_t(H.cols * 2);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   hipError_t err;
@@ -831,9 +666,9 @@ int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, in
   if (!layout(rows, cols, group, nbits, 0, &H)) return STAGQ_ESHAPE;
   if (bits < 2 || bits > nbits) return STAGQ_EBITS;
   LaunchCfg c;
-  if (!plan_gemv(H, kTileCols / group, kDepth[bits], &c)) return STAGQ_ESHAPE;
-  out[0] = c.grid; out[1] = 64 * c.waves; out[2] = c.rpp; out[3] = c.NP; out[4] = c.RB;
-  out[5] = int32_t(c.lds); out[6] = c.L; out[7] = kDepth[bits];
+  if (!plan_gemv(H, &c)) return STAGQ_ESHAPE;
+  out[0] = c.grid; out[1] = 64 * c.S; out[2] = c.S; out[3] = c.nt_max; out[4] = kBlockRows;
+  out[5] = int32_t(c.lds); out[6] = 0; out[7] = kDepth[bits];
   return STAGQ_OK;
 }
 
@@ -849,6 +684,7 @@ int stagq_decode_codes(stagq_handle h, int bits, uint8_t* codes, void* hip_strea
   p.planes = h->dev + H.off_planes;
   p.codes = codes;
   p.chunk_bytes = uint32_t(H.bytes_s0_chunk);
+  p.R = H.rows;
   p.T = H.cols / kTileCols;
   p.C = H.cols;
   p.tiles = H.tiles;

@@ -81,41 +81,42 @@ int validate_fields(const stagq_fields* f, ImageHeader* h) {
 }
 
 // Bytes one GEMV moves: base stream, planes 3..bits, group pairs, the side
-// record (8 B per entry), x and y.  (row_ptr is read only at workgroup
-// boundaries, a few KB, and is not counted.)
+// record (row_ptr and 8 B per entry), x and y.  Padding rows of the last
+// 64-row block are not counted.
 uint64_t bytes_read(const ImageHeader& h, int bits) {
   const uint64_t n = uint64_t(h.rows) * h.cols;
-  return n * 2 / 8 + n * uint64_t(bits - 2) / 8 + h.bytes_meta + uint64_t(h.nnz) * 8 +
-         uint64_t(h.cols) * 2 + uint64_t(h.rows) * 4;
+  return n * 2 / 8 + n * uint64_t(bits - 2) / 8 + uint64_t(h.rows) * (h.cols / h.group) * 4 +
+         uint64_t(h.rows + 1) * 4 + uint64_t(h.nnz) * 8 + uint64_t(h.cols) * 2 + uint64_t(h.rows) * 4;
 }
 
 // ----------------------------------------------------------------- pack ----
-static void pack_tiles(const stagq_fields* f, const ImageHeader& h, uint8_t* img, int64_t u0,
-                       int64_t u1) {
+// Writes the tiles of rows [r0, r1) (all tile columns).
+static void pack_rows(const stagq_fields* f, const ImageHeader& h, uint8_t* img, int64_t r0,
+                      int64_t r1) {
   const int64_t C = f->cols, n = int64_t(f->rows) * C, T = C / kTileCols;
-  const int N = f->nbits_max;
+  const int N = f->nbits_max, GU = kTileCols / f->group, G = C / f->group;
   uint32_t* s0a = reinterpret_cast<uint32_t*>(img + h.off_s0);
   uint32_t* s0b = reinterpret_cast<uint32_t*>(img + h.off_s0 + h.bytes_s0_chunk);
-  for (int64_t u = u0; u < u1; u++) {
-    const int64_t r = u / T, c0 = (u % T) * kTileCols;
-    const uint8_t* q = f->q + r * C + c0;
-    for (int d = 0; d < 4; d++)
-      for (int e = 0; e < 2; e++) {
-        uint32_t w = 0;
-        for (int j = 0; j < 16; j++) w |= uint32_t(q[32 * d + 2 * j + e]) << (2 * j);
-        const int dw = 2 * d + e;
-        (dw < 4 ? s0a : s0b)[u * 4 + (dw & 3)] = w;
+  uint32_t* meta = reinterpret_cast<uint32_t*>(img + h.off_meta);
+  for (int64_t r = r0; r < r1; r++)
+    for (int64_t t = 0; t < T; t++) {
+      const int64_t u = tile_index(r, t, T), c0 = t * kTileCols;
+      const uint8_t* q = f->q + r * C + c0;
+      uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int c = 0; c < kTileCols; c++) w[col_dword(c)] |= uint32_t(q[c]) << (2 * col_field(c));
+      for (int dw = 0; dw < 8; dw++) (dw < 4 ? s0a : s0b)[u * 4 + (dw & 3)] = w[dw];
+      for (int k = 3; k <= N; k++) {
+        uint32_t* pl = reinterpret_cast<uint32_t*>(img + h.off_planes + uint64_t(k - 3) * h.bytes_plane);
+        const uint8_t* b = f->planes + int64_t(k - 3) * n + r * C + c0;
+        uint32_t pw[4] = {0, 0, 0, 0};
+        for (int c = 0; c < kTileCols; c++) pw[c >> 5] |= uint32_t(b[c]) << col_plane_bit(c);
+        for (int d = 0; d < 4; d++) pl[u * 4 + d] = pw[d];
       }
-    for (int k = 3; k <= N; k++) {
-      uint32_t* pl = reinterpret_cast<uint32_t*>(img + h.off_planes + uint64_t(k - 3) * h.bytes_plane);
-      const uint8_t* b = f->planes + int64_t(k - 3) * n + r * C + c0;
-      for (int d = 0; d < 4; d++) {
-        uint32_t w = 0;
-        for (int t = 0; t < 32; t++) w |= uint32_t(b[32 * d + t]) << t;
-        pl[u * 4 + d] = w;
+      for (int gi = 0; gi < GU; gi++) {
+        const int64_t gidx = r * G + t * GU + gi;
+        meta[u * GU + gi] = uint32_t(f->lo[gidx]) | (uint32_t(f->s[gidx]) << 16);
       }
     }
-  }
 }
 
 template <class F>
@@ -145,7 +146,7 @@ const char* stagq_strerror(int status) {
     case STAGQ_OK: return "ok";
     case STAGQ_EINVAL: return "invalid argument";
     case STAGQ_EBITS: return "bits outside [2, N]";
-    case STAGQ_ESHAPE: return "unsupported shape (cols % 128, group in {32,64,128}, 2 <= N <= 8, streams < 2 GiB)";
+    case STAGQ_ESHAPE: return "unsupported shape (cols a multiple of 128 up to 32768, group in {32,64,128}, 2 <= N <= 8, streams < 2 GiB)";
     case STAGQ_ECSR: return "malformed side record";
     case STAGQ_EALIGN: return "misaligned pointer";
     case STAGQ_EHIP: return "HIP runtime error";
@@ -173,17 +174,24 @@ int stagq_pack_host(const stagq_fields* f, void* dst, size_t dst_bytes) {
   uint8_t* img = static_cast<uint8_t*>(dst);
   memset(img, 0, size_t(h.total));
   memcpy(img, &h, sizeof(h));
-  parallel_for(h.tiles, [&](int64_t a, int64_t b) { pack_tiles(f, h, img, a, b); });
+  parallel_for(f->rows, [&](int64_t a, int64_t b) { pack_rows(f, h, img, a, b); });
   const int64_t R = f->rows, G = f->cols / f->group;
-  uint32_t* meta = reinterpret_cast<uint32_t*>(img + h.off_meta);
-  for (int64_t i = 0; i < R * G; i++) meta[i] = uint32_t(f->lo[i]) | (uint32_t(f->s[i]) << 16);
   memcpy(img + h.off_rowptr, f->row_ptr, size_t(R + 1) * 4);
   uint64_t* side = reinterpret_cast<uint64_t*>(img + h.off_side);
+  uint16_t* sval = reinterpret_cast<uint16_t*>(img + h.off_sideval);
   for (int64_t r = 0; r < R; r++)
     for (int64_t e = f->row_ptr[r]; e < f->row_ptr[r + 1]; e++) {
-      const uint64_t c = uint64_t(uint32_t(f->col[e]));
-      side[e] = c | (uint64_t(f->q[r * f->cols + c]) << 30) | (uint64_t(f->val[e]) << 32) |
-                (uint64_t(r & 0xffff) << 48);
+      const int64_t c = f->col[e];
+      const int64_t gidx = r * G + c / f->group;
+      // a = P - lo - s (q - 1/2): exact in binary64 (every term is a multiple
+      // of 2^-25 below 2^18), then rounded once to binary32.
+      const double a = half_to_double(f->val[e]) - half_to_double(f->lo[gidx]) -
+                       half_to_double(f->s[gidx]) * (double(f->q[r * f->cols + c]) - 0.5);
+      const float af = float(a);
+      uint32_t abits;
+      memcpy(&abits, &af, 4);
+      side[e] = uint64_t(abits) | (uint64_t(f->s[gidx]) << 32) | (uint64_t(c) << 48);
+      sval[e] = f->val[e];
     }
   return STAGQ_OK;
 }
@@ -205,39 +213,36 @@ int stagq_unpack_host(const void* image, size_t image_bytes, stagq_info* shape, 
   shape->nnz = h.nnz; shape->image_bytes = h.total;
   for (int b = 2; b <= h.nbits; b++) shape->bytes_read[b] = bytes_read(h, b);
   const uint8_t* img = static_cast<const uint8_t*>(image);
-  const int64_t C = h.cols, T = C / kTileCols, n = int64_t(h.rows) * C;
-  if (q) {
-    const uint32_t* s0a = reinterpret_cast<const uint32_t*>(img + h.off_s0);
-    const uint32_t* s0b = reinterpret_cast<const uint32_t*>(img + h.off_s0 + h.bytes_s0_chunk);
-    for (int64_t u = 0; u < h.tiles; u++)
-      for (int dw = 0; dw < 8; dw++) {
-        const uint32_t w = (dw < 4 ? s0a : s0b)[u * 4 + (dw & 3)];
-        const int d = dw >> 1, e = dw & 1;
-        for (int j = 0; j < 16; j++)
-          q[(u / T) * C + (u % T) * kTileCols + 32 * d + 2 * j + e] = uint8_t((w >> (2 * j)) & 3);
-      }
-  }
-  if (planes)
-    for (int k = 3; k <= h.nbits; k++) {
-      const uint32_t* pl =
-          reinterpret_cast<const uint32_t*>(img + h.off_planes + uint64_t(k - 3) * h.bytes_plane);
-      for (int64_t u = 0; u < h.tiles; u++)
-        for (int d = 0; d < 4; d++)
-          for (int t = 0; t < 32; t++)
-            planes[int64_t(k - 3) * n + (u / T) * C + (u % T) * kTileCols + 32 * d + t] =
-                uint8_t((pl[u * 4 + d] >> t) & 1);
-    }
+  const int64_t R = h.rows, C = h.cols, T = C / kTileCols, n = R * C;
+  const int GU = kTileCols / h.group, G = int(C / h.group);
+  const uint32_t* s0a = reinterpret_cast<const uint32_t*>(img + h.off_s0);
+  const uint32_t* s0b = reinterpret_cast<const uint32_t*>(img + h.off_s0 + h.bytes_s0_chunk);
   const uint32_t* meta = reinterpret_cast<const uint32_t*>(img + h.off_meta);
-  const int64_t ng = int64_t(h.rows) * (C / h.group);
-  for (int64_t i = 0; i < ng; i++) {
-    if (lo) lo[i] = uint16_t(meta[i] & 0xffff);
-    if (s) s[i] = uint16_t(meta[i] >> 16);
-  }
-  if (row_ptr) memcpy(row_ptr, img + h.off_rowptr, size_t(h.rows + 1) * 4);
+  for (int64_t r = 0; r < R; r++)
+    for (int64_t t = 0; t < T; t++) {
+      const int64_t u = tile_index(r, t, T), c0 = t * kTileCols;
+      for (int c = 0; c < kTileCols; c++) {
+        const int dw = col_dword(c);
+        if (q) q[r * C + c0 + c] = uint8_t(((dw < 4 ? s0a : s0b)[u * 4 + (dw & 3)] >> (2 * col_field(c))) & 3);
+        if (planes)
+          for (int k = 3; k <= h.nbits; k++) {
+            const uint32_t* pl =
+                reinterpret_cast<const uint32_t*>(img + h.off_planes + uint64_t(k - 3) * h.bytes_plane);
+            planes[int64_t(k - 3) * n + r * C + c0 + c] = uint8_t((pl[u * 4 + (c >> 5)] >> col_plane_bit(c)) & 1);
+          }
+      }
+      for (int gi = 0; gi < GU; gi++) {
+        const uint32_t mw = meta[u * GU + gi];
+        if (lo) lo[r * G + t * GU + gi] = uint16_t(mw & 0xffff);
+        if (s) s[r * G + t * GU + gi] = uint16_t(mw >> 16);
+      }
+    }
+  if (row_ptr) memcpy(row_ptr, img + h.off_rowptr, size_t(R + 1) * 4);
   const uint64_t* side = reinterpret_cast<const uint64_t*>(img + h.off_side);
+  const uint16_t* sval = reinterpret_cast<const uint16_t*>(img + h.off_sideval);
   for (int64_t e = 0; e < h.nnz; e++) {
-    if (col) col[e] = int32_t(side[e] & 0x3fffffffu);
-    if (val) val[e] = uint16_t(side[e] >> 32);
+    if (col) col[e] = int32_t(side[e] >> 48);
+    if (val) val[e] = sval[e];
   }
   return STAGQ_OK;
 }

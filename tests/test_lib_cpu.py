@@ -77,22 +77,24 @@ def test_pack_roundtrip_and_size():
 
 def test_plane_major_layout_offsets():
     """A read at precision M touches the base stream and planes 3..M only: the
-    planes follow the base stream in order of k, each R*C/8 bytes."""
-    w, _ = synth_matrix(16, 256, "student_t", 4)
+    planes follow the base stream in order of k.  Streams hold the rows padded
+    to a multiple of 16, 16 bytes per 128-column tile."""
+    w, _ = synth_matrix(13, 256, "student_t", 4)
     F = oracle.encode(w, 128, 6, 0.0)
     img = pwo.pack_host(F)
     hdr = np.frombuffer(img[:256].tobytes(), dtype=np.uint64)
-    off_s0, off_planes = int(hdr[5]), int(hdr[6])
-    n = 16 * 256
-    assert off_planes - off_s0 >= n // 4
-    # Flipping one refinement bit in the fields changes exactly one plane's bytes.
+    off_s0, off_planes = int(hdr[6]), int(hdr[7])
+    chunk, plane = int(hdr[13]), int(hdr[14])
+    assert chunk == plane == 16 * 2 * 16        # 13 rows padded to 16, 2 tiles per row
+    assert off_planes - off_s0 == 2 * chunk
+    # Flipping one refinement bit in the fields changes exactly one byte, in plane 5.
     F2 = oracle.Fields(**{**F.__dict__})
     F2.planes = F.planes.copy()
     F2.planes[2, 3, 77] ^= 1
     img2 = pwo.pack_host(F2)
     diff = np.nonzero(img != img2)[0]
     assert diff.size == 1
-    assert off_planes + 2 * (n // 8) <= diff[0] < off_planes + 3 * (n // 8)
+    assert off_planes + 2 * plane <= diff[0] < off_planes + 3 * plane
 
 
 def test_bytes_read_model():
@@ -104,7 +106,7 @@ def test_bytes_read_model():
                                 None, None, None, None, None, None, None)
     n = 32 * 1024
     for M in (2, 3, 4):
-        want = n * M // 8 + 32 * 8 * 4 + F.nnz * 8 + 1024 * 2 + 32 * 4   # side entry: one u64
+        want = n * M // 8 + 32 * 8 * 4 + 33 * 4 + F.nnz * 8 + 1024 * 2 + 32 * 4   # row_ptr; side entry: one u64
         assert info.bytes_read[M] == want
     assert U["nnz"] == F.nnz
 
