@@ -74,7 +74,7 @@ def cpu_baseline(rows_sample: int = 1024, target_s: float = 12.0):
     w, x = synth_matrix(rows_sample, 4096, wl.dist, 0)
     F = oracle.encode(w, wl.group, wl.nbits, wl.frac, wl.ratio_T)
     G = 4096 // wl.group
-    nbytes = {M: rows_sample * 4096 * M // 8 + rows_sample * G * 4 + F.nnz * 6 + (rows_sample + 1) * 4
+    nbytes = {M: rows_sample * 4096 * M // 8 + rows_sample * G * 4 + (rows_sample + 1) * 4 + F.nnz * 8
               + 4096 * 2 + rows_sample * 4 for M in wl.bits}
     t0 = time.perf_counter()
     done = 0
@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--rot-mb", type=int, default=768, help="total size of the rotated image copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run 5 device-to-device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 (the GEMV path has "
@@ -136,6 +138,15 @@ def main():
     def launch(i, M):
         c = i % n_copies
         copies[c].gemv(xd, M, y=ys[c])
+
+    if args.calib_copy_mb:
+        # A plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters.
+        src = torch.ones(args.calib_copy_mb << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # warmup (also loads the code objects)
     for s in range(args.warmup):

@@ -25,10 +25,13 @@
 //  * Side record (Eq. 4): each entry carries a = P - lo - s (q - 1/2) and s, so
 //    its contribution (P - W_main) x_c = (a - s 2^(1-M)) x_c needs only x_c
 //    (the main stream decodes W_main = lo + s (q - 1/2 + 2^(1-M)) there because
-//    its planes are zero).  A row's entries are dealt round-robin to the 4 S
-//    lanes that hold the row, prefetched at the start, applied after the loop.
-//  * Row sums: the 4 S lane partials of a row are added in a fixed order (no
-//    atomics), so y is bitwise reproducible for a given shape and M.
+//    its planes are zero).  The block's entries (contiguous in CSR order) are
+//    spread evenly over all threads of the workgroup whatever their row, and
+//    summed per row with a segmented scan, so rows with many held-out weights
+//    cost no more than the rest.
+//  * Row sums: the 4 S lane partials of a row, then its corrections, are added
+//    in a fixed order (no atomics), so y is bitwise reproducible for a given
+//    shape and M.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -100,7 +103,8 @@ struct GemvParams {
   uint32_t chunk_bytes, meta_bytes, side_bytes, rp_bytes, x_bytes;
   int32_t R, C, T, S;      // rows, cols, tiles per row, waves (column slices) per workgroup
   int32_t g;
-  uint32_t lds_sx, lds_part;  // LDS offsets of the group sums and the row partials (x at 0)
+  uint32_t lds_sx, lds_part;  // LDS offsets of the group sums and the lane partials (x at 0)
+  uint32_t lds_rp, lds_runs;  // LDS offsets of the block's row_ptr and the side-record run sums
 };
 
 template <int M, int GU>
@@ -278,7 +282,36 @@ __device__ __forceinline__ float row_shr_add(float v) {
                                                                    0x110 + SH, 0xf, 0xf, true));
 }
 
-constexpr int kEntries = 2;    // side-record entries prefetched per lane
+// One step of a segmented inclusive scan inside 16-lane rows (DPP row_shr):
+// add the value SH lanes down when it belongs to the same segment r.
+template <int SH>
+__device__ __forceinline__ float seg_step(float v, int r) {
+  const int pv = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + SH, 0xf, 0xf, true);
+  const int pr = __builtin_amdgcn_update_dpp(-1, r, 0x110 + SH, 0xf, 0xf, false);
+  return pr == r ? v + __builtin_bit_cast(float, pv) : v;
+}
+// Carry across 16-lane rows: row_bcast:15 hands lane 15 of rows 0 / 2 to rows
+// 1 / 3 (row mask 0xa); row_bcast:31 hands lane 31 to rows 2 and 3 (mask 0xc).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float seg_bcast(float v, int r) {
+  const int pv = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xf, false);
+  const int pr = __builtin_amdgcn_update_dpp(-1, r, CTRL, ROWMASK, 0xf, false);
+  return pr == r ? v + __builtin_bit_cast(float, pv) : v;
+}
+// Segmented inclusive scan over the 64 lanes of a wave (segment ids sorted by
+// lane, every lane active): afterwards the last lane of every run of equal ids
+// holds the run's sum.
+__device__ __forceinline__ float seg_scan64(float v, int r) {
+  v = seg_step<1>(v, r);
+  v = seg_step<2>(v, r);
+  v = seg_step<4>(v, r);
+  v = seg_step<8>(v, r);
+  v = seg_bcast<0x142, 0xa>(v, r);
+  v = seg_bcast<0x143, 0xc>(v, r);
+  return v;
+}
+
+constexpr int kEntries = 2;    // side-record entries prefetched per thread
 constexpr int kXChunks = 4;    // 16-byte x chunks staged per lane: up to 4 steps per wave
 constexpr int kXPitch = 68;    // LDS dwords per tile of x: 64 + 4 of padding
 
@@ -306,12 +339,15 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   const rsrc_t rSide = mk(p.side, p.side_bytes);
   auto valid = [&](int i) { return i < nq && 4 * (q0 + i) + cg < p.T; };
 
-  // --- prologue, in arrival order: the row's side-record range, the x of this
-  //     wave's tile columns, then D steps of weights.  Nothing waits on
-  //     row_ptr before the first step.
+  // --- prologue, in arrival order: the block's row_ptr, the x of this wave's
+  //     tile columns, then D steps of weights.  Nothing waits on row_ptr
+  //     before the first step.
   const bool row_ok = r < p.R;
-  const uint32_t e0u = ld32(rRp, row_ok ? uint32_t(r) * 4u : kOOB);
-  const uint32_t e1u = ld32(rRp, row_ok ? uint32_t(r + 1) * 4u : kOOB);
+  // row_ptr of the block's 16 rows (+1) for the LDS copy (wave 0), and the
+  // block's entry range (wave-uniform, scalar loads)
+  const uint32_t rpv = ld32(rRp, w == 0 && lane <= 16 ? uint32_t(min(blk * 16 + lane, p.R)) * 4u : kOOB);
+  const int E0 = reinterpret_cast<const int*>(p.row_ptr)[min(blk * 16, p.R)];
+  const int E1 = reinterpret_cast<const int*>(p.row_ptr)[min(blk * 16 + 16, p.R)];
   const int cbase = 4 * q0 * 16;                         // first x chunk (8 columns) of the wave
   const int nch = min(4 * nq * 16, (p.C >> 3) - cbase);  // x chunks of the wave
   u32x4 xv[kXChunks];
@@ -351,17 +387,18 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     if constexpr (kCpg >= 16) { u = row_shr_add<8>(v); v = li >= 8 ? u : v; }
     sx_s[ok && li == kCpg - 1 ? ci / kCpg : p.C / p.g] = v;
   }
+  int32_t* rp_s = reinterpret_cast<int32_t*>(lds + p.lds_rp);
+  rp_s[w == 0 && lane <= 16 ? lane : 17] = int32_t(rpv);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // --- main loop; the slot of step i is reloaded with step i + D (out of
   //     range -> zeros, no traffic), which keeps every wait count
-  //     path-independent.  After the first step (row_ptr long in) the lane's
-  //     first side-record entries are requested: entries e0 + j with
-  //     j = 4 w + cg modulo 4 S, applied after the loop.
-  const int stride = 4 * p.S;
-  int e0 = 0, e1 = 0;
+  //     path-independent.  After the first step the thread's first
+  //     side-record entries of the block are requested: entries
+  //     E0 + j * threads + thread id, applied after the loop.
+  const int tid = threadIdx.x, nthr = blockDim.x;
   uint64_t ent[kEntries];
   float part = 0.f;
   auto step = [&](Slot<M, GU>& s, int i) {
@@ -375,12 +412,10 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     __builtin_amdgcn_sched_barrier(0);   // reuse the slot's registers: no loads hoisted above
     issue(s, rW, chunk, rMeta, ubase + uint32_t(i + D) * 64u, valid(i + D));
     if (i == 0) {
-      e0 = int(e0u) + 4 * w + cg;
-      e1 = int(e1u);
 #pragma unroll
       for (int j = 0; j < kEntries; j++) {
-        const int e = e0 + j * stride;
-        ent[j] = ld64side(rSide, e < e1 ? uint32_t(e) * 8u : kOOB);
+        const int e = E0 + j * nthr + tid;
+        ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
       }
     }
   };
@@ -390,32 +425,65 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
 #pragma unroll
     for (int i = 0; i < D; i++) step(sl[i], ib + i);
   }
-  __syncthreads();                       // x complete in LDS
-
-  // --- this lane's side-record corrections (a - s 2^(1-M)) x_c, in entry order.
-  constexpr float kHalfUlp = 2.0f / float(1 << M);   // 2^(1-M)
-  const uint16_t* xh = reinterpret_cast<const uint16_t*>(xs);
-  auto corr = [&](uint64_t ev) -> float {
-    const float a = __builtin_bit_cast(float, uint32_t(ev));
-    const float st = h2f(uint32_t(ev >> 32) & 0xffffu);
-    const int c = int(ev >> 48);
-    return (a - st * kHalfUlp) * h2f(xh[(c >> 7) * (2 * kXPitch) + (c & 127)]);
-  };
-#pragma unroll
-  for (int j = 0; j < kEntries; j++)
-    if (e0 + j * stride < e1) part += corr(ent[j]);
-  for (int e = e0 + kEntries * stride; e < e1; e += stride) part += corr(ld64side(rSide, uint32_t(e) * 8u));
-
-  // --- row sums: lane partials in (wave, tile column) order.
   part_s[w * 64 + lane] = part;
-  __syncthreads();
-  if (w == 0 && lane < 16 && row_ok) {
-    float acc = 0.f;
+  __syncthreads();                       // x and the block's row_ptr complete in LDS
+
+  // --- row sums: lane partials in (wave, tile column) order ...
+  float acc = 0.f;
+  const bool owner = w == 0 && lane < 16;
+  if (owner) {
     for (int k = 0; k < p.S; k++)
 #pragma unroll
       for (int c = 0; c < 4; c++) acc += part_s[k * 64 + c * 16 + lane];
-    p.y[r] = acc;
   }
+
+  // --- ... then the side-record corrections (a - s 2^(1-M)) x_c of the block,
+  //     in entry order.  A chunk of kEntries * threads entries is spread over
+  //     the threads (64 consecutive entries per wave and j); a segmented scan
+  //     by row leaves, at the last lane of every row run, the run's sum; the
+  //     row's owner adds its runs in order.
+  constexpr float kHalfUlp = 2.0f / float(1 << M);   // 2^(1-M)
+  const uint16_t* xh = reinterpret_cast<const uint16_t*>(xs);
+  float* runs_s = reinterpret_cast<float*>(lds + p.lds_runs);
+  const int echunk = kEntries * nthr;
+  for (int cb = E0; cb < E1; cb += echunk) {
+    if (cb > E0) {                       // rare: more entries than one prefetched chunk
+      __syncthreads();                   // the previous chunk's runs are consumed
+#pragma unroll
+      for (int j = 0; j < kEntries; j++) {
+        const int e = cb + j * nthr + tid;
+        ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kEntries; j++) {
+      const int e = cb + j * nthr + tid;
+      const bool ok = e < E1;
+      int seg = 16;                      // rows of the block 0..15; 16 = no entry
+      float v = 0.f;
+      if (ok) {
+        seg = 0;
+#pragma unroll
+        for (int i = 1; i < 16; i++) seg += e >= rp_s[i] ? 1 : 0;
+        const uint64_t ev = ent[j];
+        const float a = __builtin_bit_cast(float, uint32_t(ev));
+        const float st = h2f(uint32_t(ev >> 32) & 0xffffu);
+        const int c = int(ev >> 48);
+        v = (a - st * kHalfUlp) * h2f(xh[(c >> 7) * (2 * kXPitch) + (c & 127)]);
+      }
+      v = seg_scan64(v, seg);
+      const int nseg = __shfl_down(seg, 1);
+      const bool last = lane == 63 || nseg != seg;
+      runs_s[(j * p.S + w) * 17 + (last ? seg : 16)] = v;
+    }
+    __syncthreads();
+    if (owner) {
+      // the row's entries in this chunk: [max(rp, cb), min(rp+1, cb + chunk))
+      const int a = max(rp_s[lane], cb) - cb, b = min(rp_s[lane + 1], cb + echunk) - cb;
+      for (int q = a; q < b; q = (q | 63) + 1) acc += runs_s[(q >> 6) * 17 + lane];
+    }
+  }
+  if (owner && row_ok) p.y[r] = acc;
 }
 
 // Code dump: one thread per (padded) tile writes the 128 codes u_M (Eq. 8) of
@@ -503,7 +571,8 @@ constexpr int kDepth[9] = {0, 0, 4, 4, 3, 3, 2, 2, 2};
 constexpr int kMaxWaves = 16;   // matches __launch_bounds__(1024) of the GEMV kernel
 
 // LDS carve-up: x padded to 68 dwords per tile (plus a spare chunk), sum(x)
-// per group (plus a spare slot), per-wave lane partials.
+// per group (plus a spare slot), per-wave lane partials, the block's row_ptr
+// (plus a spare slot), side-record run sums (17 per 64-entry batch).
 static size_t lds_layout(int C, int g, int S, dev::GemvParams* prm) {
   size_t o = size_t(C / kTileCols + 1) * dev::kXPitch * 4;
   if (prm) prm->lds_sx = uint32_t(o);
@@ -511,6 +580,11 @@ static size_t lds_layout(int C, int g, int S, dev::GemvParams* prm) {
   o = (o + 15) & ~size_t(15);
   if (prm) prm->lds_part = uint32_t(o);
   o += size_t(S) * 64 * 4;
+  if (prm) prm->lds_rp = uint32_t(o);
+  o += 18 * 4;
+  o = (o + 15) & ~size_t(15);
+  if (prm) prm->lds_runs = uint32_t(o);
+  o += size_t(dev::kEntries) * S * 17 * 4;
   return o;
 }
 
