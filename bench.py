@@ -94,6 +94,76 @@ def cpu_baseline(rows_sample: int = 1024, target_s: float = 12.0):
     }
 
 
+def graph_time(launch, n_copies, K, bits_seq):
+    """Mean microseconds per launch of K launches captured in one HIP graph
+    (launch i uses copy i % n_copies and precision bits_seq[i % len(bits_seq)])."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(K):
+            launch(i % n_copies, bits_seq[i % len(bits_seq)])
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / K
+
+
+def sweep(args):
+    """Every matrix of the attention, MLP, Phi-4 and layer-sweep workloads at each
+    precision (one graph of K launches per precision, rotating image copies),
+    plus the layer sweep's per-call precision switching 2, 3, 4, 2, ...; one JSON line."""
+    import torch
+    import precision_weight_only_amd as pwo
+    from workloads import WORKLOADS, synth_matrix
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows = []
+    for wname in ("attn", "mlp", "phi4_mlp", "layer_sweep"):
+        wl = WORKLOADS[wname]
+        for mat in wl.matrices:
+            w, x = synth_matrix(mat.rows, mat.cols, wl.dist, mat.seed)
+            K = int(np.floor(wl.frac * mat.rows * mat.cols + 0.5))
+            fields = pwo.encode(w, wl.group, wl.nbits, K, wl.ratio_T)
+            del w
+            base = pwo.StagQMatrix.pack(fields, device=dev)
+            del fields
+            n_copies = max(2, -(-args.rot_mb * (1 << 20) // base.image_bytes))
+            copies = [base] + [base.replicate() for _ in range(n_copies - 1)]
+            xd = torch.from_numpy(x.view(np.int16)).view(torch.float16).to(dev)
+            ys = [torch.empty(mat.rows, dtype=torch.float32, device=dev) for _ in range(n_copies)]
+
+            def launch(c, M):
+                copies[c].gemv(xd, M, y=ys[c])
+
+            for i in range(args.warmup):
+                launch(i % n_copies, wl.bits[i % len(wl.bits)])
+            torch.cuda.synchronize()
+            entry = {"workload": wname, "matrix": mat.name, "rows": mat.rows, "cols": mat.cols,
+                     "nnz": int(base.nnz), "copies": n_copies, "bits": {}}
+            for M in wl.bits:
+                us = graph_time(launch, n_copies, args.steps, [M])
+                b = base.bytes_read[M]
+                entry["bits"][str(M)] = {"us": round(us, 3), "bytes": int(b), "gbps": round(b / us / 1e3, 1),
+                                         "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2),
+                                         "launch": pwo.plan_gemv(mat.rows, mat.cols, wl.group, wl.nbits, M)}
+            if wname == "layer_sweep":
+                us = graph_time(launch, n_copies, args.steps, list(wl.bits))
+                b = sum(base.bytes_read[M] for M in wl.bits) / len(wl.bits)
+                entry["switched_2_3_4"] = {"us_per_call": round(us, 3), "gbps": round(b / us / 1e3, 1)}
+            rows.append(entry)
+            print(f"[sweep] {wname}/{mat.name} {mat.rows}x{mat.cols}: " +
+                  " ".join(f"{M}b {v['us']}us {v['pct_peak']}%" for M, v in entry["bits"].items()),
+                  file=sys.stderr, flush=True)
+            del copies, base, ys
+            torch.cuda.empty_cache()
+    print(json.dumps({"metric": METRIC, "sweep": rows, "steps": args.steps, "warmup": args.warmup,
+                      "mode": "graph", "data": "synthetic"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +172,8 @@ def main():
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--rot-mb", type=int, default=768, help="total size of the rotated image copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every matrix of every workload instead of the headline line")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run 5 device-to-device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -115,6 +187,9 @@ def main():
     from workloads import WORKLOADS, synth_matrix
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.sweep:
+        sweep(args)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = WORKLOADS["mlp"]

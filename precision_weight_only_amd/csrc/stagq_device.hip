@@ -340,14 +340,11 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   auto valid = [&](int i) { return i < nq && 4 * (q0 + i) + cg < p.T; };
 
   // --- prologue, in arrival order: the block's row_ptr, the x of this wave's
-  //     tile columns, then D steps of weights.  Nothing waits on row_ptr
-  //     before the first step.
+  //     tile columns, then D steps of weights.
   const bool row_ok = r < p.R;
-  // row_ptr of the block's 16 rows (+1) for the LDS copy (wave 0), and the
-  // block's entry range (wave-uniform, scalar loads)
-  const uint32_t rpv = ld32(rRp, w == 0 && lane <= 16 ? uint32_t(min(blk * 16 + lane, p.R)) * 4u : kOOB);
-  const int E0 = reinterpret_cast<const int*>(p.row_ptr)[min(blk * 16, p.R)];
-  const int E1 = reinterpret_cast<const int*>(p.row_ptr)[min(blk * 16 + 16, p.R)];
+  // row_ptr of the block's 16 rows (+1): the block's entry range, and the LDS
+  // copy used to find an entry's row
+  const uint32_t rpv = ld32(rRp, lane <= 16 ? uint32_t(min(blk * 16 + lane, p.R)) * 4u : kOOB);
   const int cbase = 4 * q0 * 16;                         // first x chunk (8 columns) of the wave
   const int nch = min(4 * nq * 16, (p.C >> 3) - cbase);  // x chunks of the wave
   u32x4 xv[kXChunks];
@@ -364,6 +361,19 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  // --- the thread's first side-record entries of the block (entries
+  //     E0 + j * threads + thread id, applied after the loop).  Waiting for
+  //     row_ptr here costs nothing: it is the wave's first load and the x
+  //     below is waited for right after.
+  const int tid = threadIdx.x, nthr = 64 * p.S;
+  const int E0 = __builtin_amdgcn_readlane(int(rpv), 0), E1 = __builtin_amdgcn_readlane(int(rpv), 16);
+  uint64_t ent[kEntries];
+#pragma unroll
+  for (int j = 0; j < kEntries; j++) {
+    const int e = E0 + j * nthr + tid;
+    ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
+  }
+
   // --- this wave's x into LDS, and sum(x) per group: a chunk holds 8
   //     columns, a group 16 / GU consecutive chunks = lanes of one DPP row,
   //     summed with row_shr steps.  Spare lanes write to spare slots so no load
@@ -372,6 +382,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   const int li = lane & (kCpg - 1);
 #pragma unroll
   for (int k = 0; k < kXChunks; k++) {
+    if (64 * k >= nch) break;            // the wave's x ends here (uniform)
     const int c = lane + 64 * k;
     const bool ok = c < nch;
     const int ci = cbase + c;
@@ -395,11 +406,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
 
   // --- main loop; the slot of step i is reloaded with step i + D (out of
   //     range -> zeros, no traffic), which keeps every wait count
-  //     path-independent.  After the first step the thread's first
-  //     side-record entries of the block are requested: entries
-  //     E0 + j * threads + thread id, applied after the loop.
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  uint64_t ent[kEntries];
+  //     path-independent.
   float part = 0.f;
   auto step = [&](Slot<M, GU>& s, int i) {
     if (i < nq) {
@@ -411,13 +418,6 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);   // reuse the slot's registers: no loads hoisted above
     issue(s, rW, chunk, rMeta, ubase + uint32_t(i + D) * 64u, valid(i + D));
-    if (i == 0) {
-#pragma unroll
-      for (int j = 0; j < kEntries; j++) {
-        const int e = E0 + j * nthr + tid;
-        ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
-      }
-    }
   };
 #pragma unroll
   for (int i = 0; i < D; i++) step(sl[i], i);
@@ -457,6 +457,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     }
 #pragma unroll
     for (int j = 0; j < kEntries; j++) {
+      if (cb + j * nthr >= E1) break;    // no entries left in the block (uniform)
       const int e = cb + j * nthr + tid;
       const bool ok = e < E1;
       int seg = 16;                      // rows of the block 0..15; 16 = no entry
