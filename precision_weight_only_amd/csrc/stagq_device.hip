@@ -566,9 +566,12 @@ static int env_int(const char* name, int dflt) {
   return e ? atoi(e) : dflt;
 }
 
-// Tile columns of loads in flight per wave, per precision (bounded by the
-// VGPRs of a slot: 8 + 4 (M - 2) + pairs dwords).
-constexpr int kDepth[9] = {0, 0, 4, 4, 3, 3, 2, 2, 2};
+// Steps of loads in flight per wave, per precision.  Shallow on purpose: with
+// two to four waves per SIMD the chip holds enough bytes in flight, and
+// deeper per-wave queues only delay every wave's first data (measured on the
+// 14336 x 4096 and 4096 x 14336 shapes: depth 2 beats 3 and 4 at two bits,
+// depth 1 beats 2 at four bits).
+constexpr int kDepth[9] = {0, 0, 2, 2, 1, 1, 1, 1, 1};
 constexpr int kMaxWaves = 16;   // matches __launch_bounds__(1024) of the GEMV kernel
 
 // LDS carve-up: x padded to 68 dwords per tile (plus a spare chunk), sum(x)
