@@ -146,10 +146,11 @@ int stagq_decode_codes(stagq_handle h, int bits, uint8_t* codes, void* hip_strea
  * Launch shape the GEMV uses for a matrix of this shape at precision bits (on
  * the current device, or assuming 256 compute units when none is present):
  * out[0] workgroups (one per 16-row block), out[1] threads per workgroup,
- * out[2] waves per workgroup, out[3] steps per wave (a step is 16 rows x 4
- * tile columns of 128), out[4] rows per workgroup, out[5] LDS bytes, out[6]
- * reserved (0), out[7] steps of loads in flight per wave.  out is host
- * int32[8].  Pure host logic.
+ * out[2] waves per workgroup that stream the main stream, out[3] steps per
+ * such wave (a step is 16 rows x 4 tile columns of 128), out[4] rows per
+ * workgroup, out[5] LDS bytes, out[6] 1 if the side record runs on an extra
+ * wave of each workgroup (else 0), out[7] steps of loads in flight per wave.
+ * out is host int32[8].  Pure host logic.
  */
 int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int bits,
                     int32_t* out);

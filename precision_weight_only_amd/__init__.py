@@ -66,7 +66,7 @@ def plan_gemv(rows: int, cols: int, group: int, nbits: int, bits: int) -> Dict[s
     check(lib().stagq_plan_gemv(rows, cols, group, nbits, bits, C.cast(out, C.c_void_p)),
           "stagq_plan_gemv")
     keys = ("grid", "threads", "waves", "steps_per_wave", "rows_per_group", "lds_bytes",
-            "reserved", "depth")
+            "side_wave", "depth")
     return dict(zip(keys, list(out)))
 
 

@@ -311,40 +311,109 @@ __device__ __forceinline__ float seg_scan64(float v, int r) {
   return v;
 }
 
-constexpr int kEntries = 2;    // side-record entries prefetched per thread
-constexpr int kXChunks = 4;    // 16-byte x chunks staged per lane: up to 4 steps per wave
-constexpr int kXPitch = 68;    // LDS dwords per tile of x: 64 + 4 of padding
+constexpr int kEntries = 2;      // side-record entries prefetched per thread (in-workgroup mode)
+constexpr int kSideBatches = 8;  // 64-entry batches the side-record wave keeps in flight
+constexpr int kXChunks = 4;      // 16-byte x chunks staged per lane: up to 4 steps per wave
+constexpr int kXPitch = 68;      // LDS dwords per tile of x: 64 + 4 of padding
 
-template <int M, int GU, int D>
+// Side-record wave (SIDE mode): the side record of one 16-row block, run by
+// the workgroup's extra wave while the others stream the main stream.
+// row_ptr -> entries -> x_c are three dependent loads, and this wave issues no
+// others, so its waits never queue behind weight traffic.  The block's entries
+// (contiguous in CSR order) go 64 per batch, up to kSideBatches batches in
+// flight; per batch a segmented scan by row leaves each row run's sum at its
+// last lane, which adds it to the row's total in LDS (batches in order: a fixed
+// summation order).
+template <int M>
+__device__ __forceinline__ void side_record(const GemvParams& p, int blk, int lane, int32_t* rp_s,
+                                            float* rowc_s, const rsrc_t& rRp, const rsrc_t& rSide,
+                                            const rsrc_t& rX) {
+  constexpr float kHalfUlp = 2.0f / float(1 << M);   // 2^(1-M)
+  const uint32_t rpv = ld32(rRp, lane <= 16 ? uint32_t(min(blk * 16 + lane, p.R)) * 4u : kOOB);
+  if (lane < 16) rowc_s[lane] = 0.f;
+  const int E0 = __builtin_amdgcn_readlane(int(rpv), 0), E1 = __builtin_amdgcn_readlane(int(rpv), 16);
+  if (lane <= 16) rp_s[lane] = int32_t(rpv);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int cb = E0; cb < E1; cb += 64 * kSideBatches) {
+    uint64_t ent[kSideBatches];
+#pragma unroll
+    for (int j = 0; j < kSideBatches; j++) {
+      const int e = cb + 64 * j + lane;
+      ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
+    }
+    uint32_t xc[kSideBatches];
+#pragma unroll
+    for (int j = 0; j < kSideBatches; j++) {
+      const int e = cb + 64 * j + lane;
+      xc[j] = ld16(rX, e < E1 ? uint32_t(ent[j] >> 48) * 2u : kOOB);
+    }
+#pragma unroll
+    for (int j = 0; j < kSideBatches; j++) {
+      if (cb + 64 * j >= E1) break;      // no entries left in the block (uniform)
+      const int e = cb + 64 * j + lane;
+      const bool ok = e < E1;
+      // row of entry e within the block: the last i with row_ptr[i] <= e
+      int seg = 0;
+#pragma unroll
+      for (int st = 8; st >= 1; st >>= 1) seg += e >= rp_s[seg + st] ? st : 0;
+      seg = ok ? seg : 16;               // 16 = no entry
+      const uint64_t ev = ent[j];
+      const float a = __builtin_bit_cast(float, uint32_t(ev));
+      const float st = h2f(uint32_t(ev >> 32) & 0xffffu);
+      float v = ok ? (a - st * kHalfUlp) * h2f(xc[j]) : 0.f;
+      v = seg_scan64(v, seg);
+      const int nseg = __shfl_down(seg, 1);
+      if ((lane == 63 || nseg != seg) && ok) rowc_s[seg] += v;
+    }
+  }
+}
+
+// The GEMV.  SIDE selects where the side record is applied: by an extra wave
+// of the workgroup (SIDE = 1, for grids with several workgroups per CU, where
+// its latency hides behind other workgroups) or by all waves after the main
+// loop (SIDE = 0).
+template <int M, int GU, int D, int SIDE>
 __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
   uint32_t* xs = reinterpret_cast<uint32_t*>(lds);            // x pairs, tile t at t * kXPitch
   float* sx_s = reinterpret_cast<float*>(lds + p.lds_sx);     // sum(x) per group
   float* part_s = reinterpret_cast<float*>(lds + p.lds_part); // lane partials per wave
+  int32_t* rp_s = reinterpret_cast<int32_t*>(lds + p.lds_rp); // the block's row_ptr (+ spare)
+  float* runs_s = reinterpret_cast<float*>(lds + p.lds_runs); // run sums / side total per row
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int blk = blockIdx.x;
-  const int cg = lane >> 4;                       // tile column within the four
   const int r = blk * 16 + (lane & 15);
-  const int Q = (p.T + 3) >> 2;                    // groups of four tile columns
-  const int q0 = (w * Q) / p.S, nq = ((w + 1) * Q) / p.S - q0;
-  const uint32_t ubase = uint32_t(blk * p.T + 4 * q0) * 16u + uint32_t(lane);  // tile of step 0
-
-  const uint32_t chunk = p.chunk_bytes;
-  const rsrc_t rW = mk(p.s0, uint32_t(M) * chunk);
-  const rsrc_t rMeta = mk(p.meta, p.meta_bytes);
+  const bool row_ok = r < p.R;
   const rsrc_t rX = mk(p.x, p.x_bytes);
   const rsrc_t rRp = mk(p.row_ptr, p.rp_bytes);
   const rsrc_t rSide = mk(p.side, p.side_bytes);
+
+  if constexpr (SIDE) {
+    if (w == p.S) {                      // the side-record wave
+      side_record<M>(p, blk, lane, rp_s, runs_s, rRp, rSide, rX);
+      __syncthreads();
+      return;
+    }
+  }
+
+  const int cg = lane >> 4;                       // tile column within the four
+  const int Q = (p.T + 3) >> 2;                    // groups of four tile columns
+  const int q0 = (w * Q) / p.S, nq = ((w + 1) * Q) / p.S - q0;
+  const uint32_t ubase = uint32_t(blk * p.T + 4 * q0) * 16u + uint32_t(lane);  // tile of step 0
+  const uint32_t chunk = p.chunk_bytes;
+  const rsrc_t rW = mk(p.s0, uint32_t(M) * chunk);
+  const rsrc_t rMeta = mk(p.meta, p.meta_bytes);
   auto valid = [&](int i) { return i < nq && 4 * (q0 + i) + cg < p.T; };
 
-  // --- prologue, in arrival order: the block's row_ptr, the x of this wave's
-  //     tile columns, then D steps of weights.
-  const bool row_ok = r < p.R;
-  // row_ptr of the block's 16 rows (+1): the block's entry range, and the LDS
-  // copy used to find an entry's row
-  const uint32_t rpv = ld32(rRp, lane <= 16 ? uint32_t(min(blk * 16 + lane, p.R)) * 4u : kOOB);
+  // --- prologue, in arrival order: (in-workgroup mode) the block's row_ptr,
+  //     the x of this wave's tile columns, then D steps of weights.
+  uint32_t rpv = 0;
+  if constexpr (!SIDE)
+    rpv = ld32(rRp, lane <= 16 ? uint32_t(min(blk * 16 + lane, p.R)) * 4u : kOOB);
   const int cbase = 4 * q0 * 16;                         // first x chunk (8 columns) of the wave
   const int nch = min(4 * nq * 16, (p.C >> 3) - cbase);  // x chunks of the wave
   u32x4 xv[kXChunks];
@@ -361,17 +430,21 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // --- the thread's first side-record entries of the block (entries
-  //     E0 + j * threads + thread id, applied after the loop).  Waiting for
-  //     row_ptr here costs nothing: it is the wave's first load and the x
-  //     below is waited for right after.
+  // --- (in-workgroup mode) the thread's first side-record entries of the
+  //     block: entries E0 + j * threads + thread id, applied after the loop.
+  //     Waiting for row_ptr here costs nothing: it is the wave's first load and
+  //     the x below is waited for right after.
   const int tid = threadIdx.x, nthr = 64 * p.S;
-  const int E0 = __builtin_amdgcn_readlane(int(rpv), 0), E1 = __builtin_amdgcn_readlane(int(rpv), 16);
+  int E0 = 0, E1 = 0;
   uint64_t ent[kEntries];
+  if constexpr (!SIDE) {
+    E0 = __builtin_amdgcn_readlane(int(rpv), 0);
+    E1 = __builtin_amdgcn_readlane(int(rpv), 16);
 #pragma unroll
-  for (int j = 0; j < kEntries; j++) {
-    const int e = E0 + j * nthr + tid;
-    ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
+    for (int j = 0; j < kEntries; j++) {
+      const int e = E0 + j * nthr + tid;
+      ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
+    }
   }
 
   // --- this wave's x into LDS, and sum(x) per group: a chunk holds 8
@@ -398,8 +471,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     if constexpr (kCpg >= 16) { u = row_shr_add<8>(v); v = li >= 8 ? u : v; }
     sx_s[ok && li == kCpg - 1 ? ci / kCpg : p.C / p.g] = v;
   }
-  int32_t* rp_s = reinterpret_cast<int32_t*>(lds + p.lds_rp);
-  rp_s[w == 0 && lane <= 16 ? lane : 17] = int32_t(rpv);
+  if constexpr (!SIDE) rp_s[w == 0 && lane <= 16 ? lane : 17] = int32_t(rpv);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -425,8 +497,9 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
 #pragma unroll
     for (int i = 0; i < D; i++) step(sl[i], ib + i);
   }
+
   part_s[w * 64 + lane] = part;
-  __syncthreads();                       // x and the block's row_ptr complete in LDS
+  __syncthreads();                       // partials (and x, row_ptr or side totals) complete in LDS
 
   // --- row sums: lane partials in (wave, tile column) order ...
   float acc = 0.f;
@@ -436,15 +509,20 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
 #pragma unroll
       for (int c = 0; c < 4; c++) acc += part_s[k * 64 + c * 16 + lane];
   }
+  if constexpr (SIDE) {
+    // ... then the row's side-record total from the side-record wave.
+    if (owner && row_ok) p.y[r] = acc + runs_s[lane];
+    return;
+  }
 
-  // --- ... then the side-record corrections (a - s 2^(1-M)) x_c of the block,
-  //     in entry order.  A chunk of kEntries * threads entries is spread over
-  //     the threads (64 consecutive entries per wave and j); a segmented scan
-  //     by row leaves, at the last lane of every row run, the run's sum; the
-  //     row's owner adds its runs in order.
+  // --- ... then (in-workgroup mode) the side-record corrections
+  //     (a - s 2^(1-M)) x_c of the block, in entry order.  A chunk of
+  //     kEntries * threads entries is spread over the threads (64 consecutive
+  //     entries per wave and j); a segmented scan by row leaves, at the last
+  //     lane of every row run, the run's sum; the row's owner adds its runs in
+  //     order.
   constexpr float kHalfUlp = 2.0f / float(1 << M);   // 2^(1-M)
   const uint16_t* xh = reinterpret_cast<const uint16_t*>(xs);
-  float* runs_s = reinterpret_cast<float*>(lds + p.lds_runs);
   const int echunk = kEntries * nthr;
   for (int cb = E0; cb < E1; cb += echunk) {
     if (cb > E0) {                       // rare: more entries than one prefetched chunk
@@ -535,6 +613,7 @@ __global__ void __launch_bounds__(256) codes_kernel(const CodesParams p) {
 // ------------------------------------------------------------- dispatch ----
 struct LaunchCfg {
   int S, grid, nt_max;
+  bool side;                    // side record on an extra wave (SIDE mode)
   size_t lds;
   dev::GemvParams prm;
 };
@@ -572,7 +651,7 @@ static int env_int(const char* name, int dflt) {
 // 14336 x 4096 and 4096 x 14336 shapes: depth 2 beats 3 and 4 at two bits,
 // depth 1 beats 2 at four bits).
 constexpr int kDepth[9] = {0, 0, 2, 2, 1, 1, 1, 1, 1};
-constexpr int kMaxWaves = 16;   // matches __launch_bounds__(1024) of the GEMV kernel
+constexpr int kMaxWaves = 16;   // waves per workgroup (incl. a side-record wave): __launch_bounds__(1024)
 
 // LDS carve-up: x padded to 68 dwords per tile (plus a spare chunk), sum(x)
 // per group (plus a spare slot), per-wave lane partials, the block's row_ptr
@@ -595,22 +674,30 @@ static size_t lds_layout(int C, int g, int S, dev::GemvParams* prm) {
 // Launch shape: one workgroup per 16-row block, S waves splitting the row's
 // groups of four tile columns.  S is the smallest count that puts about two
 // waves on every SIMD (8 per CU), within [ceil(groups / 4), min(16, groups)]
-// (a wave stages the x of at most 4 steps).  STAGQ_WAVES overrides the choice
-// (tuning).
+// (a wave stages the x of at most 4 steps).  With at least two workgroups per
+// CU the side record goes to an extra wave (its latency then hides behind
+// other workgroups; with fewer it would sit on the critical path).
+// STAGQ_WAVES and STAGQ_SIDE override the choices (tuning).
 static bool plan_gemv(const ImageHeader& h, LaunchCfg* c) {
   const int T = h.cols / kTileCols;
   const int Q = (T + 3) / 4;
   const int nblk = h.blocks;
+  if (nblk <= 0) return false;
+  const int cus = device_cus();
+  bool side = nblk >= 2 * cus;
+  const int side_env = env_int("STAGQ_SIDE", -1);
+  if (side_env == 0 || side_env == 1) side = side_env == 1;
   const int smin = (Q + dev::kXChunks - 1) / dev::kXChunks;
-  const int smax = std::min(kMaxWaves, Q);
-  if (nblk <= 0 || smin > smax) return false;
-  const int target = 2 * 4 * device_cus();
+  const int smax = std::min(kMaxWaves - (side ? 1 : 0), Q);
+  if (smin > smax) return false;
+  const int target = 2 * 4 * cus;
   int S = (target + nblk - 1) / nblk;
   S = std::max(smin, std::min(smax, S));
   const int s_env = env_int("STAGQ_WAVES", 0);
   if (s_env) S = s_env;
   if (S < smin || S > smax) return false;
   c->S = S;
+  c->side = side;
   c->grid = nblk;
   c->nt_max = (Q + S - 1) / S;
   c->lds = lds_layout(h.cols, h.group, S, &c->prm);
@@ -621,7 +708,10 @@ static bool plan_gemv(const ImageHeader& h, LaunchCfg* c) {
 
 template <int M, int GU, int D>
 static hipError_t launch_gemv(const LaunchCfg& c, hipStream_t st) {
-  hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D>), dim3(c.grid), dim3(64 * c.S), c.lds, st, c.prm);
+  if (c.side)
+    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 1>), dim3(c.grid), dim3(64 * (c.S + 1)), c.lds, st, c.prm);
+  else
+    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 0>), dim3(c.grid), dim3(64 * c.S), c.lds, st, c.prm);
   return hipGetLastError();
 }
 
@@ -745,8 +835,8 @@ int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, in
   if (bits < 2 || bits > nbits) return STAGQ_EBITS;
   LaunchCfg c;
   if (!plan_gemv(H, &c)) return STAGQ_ESHAPE;
-  out[0] = c.grid; out[1] = 64 * c.S; out[2] = c.S; out[3] = c.nt_max; out[4] = kBlockRows;
-  out[5] = int32_t(c.lds); out[6] = 0; out[7] = kDepth[bits];
+  out[0] = c.grid; out[1] = 64 * (c.S + (c.side ? 1 : 0)); out[2] = c.S; out[3] = c.nt_max;
+  out[4] = kBlockRows; out[5] = int32_t(c.lds); out[6] = c.side ? 1 : 0; out[7] = kDepth[bits];
   return STAGQ_OK;
 }
 

@@ -245,3 +245,18 @@ def test_error_codes(pwo):
     with pytest.raises(pwo.StagQError) as e:
         m.decode_codes(7)
     assert e.value.status == -2
+
+
+@pytest.mark.parametrize("side", ["0", "1"])
+def test_side_record_modes(pwo, side, monkeypatch):
+    """Both places the side record can be applied (all waves after the main
+    loop, or an extra wave of the workgroup; the library picks one per shape)
+    meet the parity bar on small and skewed side records."""
+    monkeypatch.setenv("STAGQ_SIDE", side)
+    F, x = _encoded("tiny", "W")
+    _check(pwo, F, x, (2, 3, 4), f"tiny side={side}")
+    for case in ((1001, 384, 64, 4, 0.01, "student_t", 2), (77, 640, 32, 6, 0.02, "normal_outliers", 3),
+                 (64, 4096, 128, 4, 0.1, "student_t", 5)):
+        R, Cc, g, N, frac, dist, seed = case
+        w, xe = synth_matrix(R, Cc, dist, seed)
+        _check(pwo, oracle.encode(w, g, N, frac), xe, range(2, N + 1), f"edge{case} side={side}")
