@@ -68,9 +68,20 @@ __device__ __forceinline__ uint32_t ld16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c, false);
 }
+// dot2 into a zero accumulator: one VOP3P instruction with an inline 0, not a
+// move of 0 followed by the accumulating form.
+__device__ __forceinline__ float dot2z(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
   return (a & m) | (b & ~m);
 }
+// Pin a word as computed (one register, one bit-field insert): without it the
+// compiler distributes the masks applied later into the inserts that built
+// the word, which costs more instructions than the insert it saves.
+__device__ __forceinline__ void keep(uint32_t& v) { asm("" : "+v"(v)); }
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
@@ -85,12 +96,14 @@ __device__ __forceinline__ uint64_t ld64side(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void pair_fields(uint32_t phi, uint32_t plo, uint32_t& ev, uint32_t& od) {
   ev = bfi(0x55555555u, plo, phi << 1);
   od = bfi(0xAAAAAAAAu, phi, plo >> 1);
+  keep(ev); keep(od);
 }
 // 4-bit codes from a high 2-bit field word and a low 2-bit field word:
 // nibble m of zlo / zhi is the code of field 2m / 2m+1.
 __device__ __forceinline__ void nibbles(uint32_t hw, uint32_t lw, uint32_t& zlo, uint32_t& zhi) {
   zlo = bfi(0x33333333u, lw, hw << 2);
   zhi = bfi(0xCCCCCCCCu, hw, lw >> 2);
+  keep(zlo); keep(zhi);
 }
 
 struct GemvParams {
@@ -103,7 +116,7 @@ struct GemvParams {
   uint32_t chunk_bytes, meta_bytes, side_bytes, rp_bytes, x_bytes;
   int32_t R, C, T, S;      // rows, cols, tiles per row, waves (column slices) per workgroup
   int32_t g;
-  uint32_t lds_sx, lds_part;  // LDS offsets of the group sums and the lane partials (x at 0)
+  uint32_t lds_part;          // LDS offset of the lane partials (x and sum(x) at 0)
   uint32_t lds_rp, lds_runs;  // LDS offsets of the block's row_ptr and the side-record run sums
 };
 
@@ -142,25 +155,35 @@ __device__ __forceinline__ uint32_t s0_dword(const u32x4& a, const u32x4& b, int
 }
 
 // Products of one 32-column quarter d of a tile (S0 dwords 2d, 2d+1, plane
-// dwords d) with its x pairs xq[0..15]; accumulators of the quarter.
-template <int M, int GU>
+// dwords d) with its x pairs xq[0..15]; accumulators of the quarter, which
+// start from zero when FIRST (the quarter opens a group).
+template <int M, int GU, bool FIRST>
 __device__ __forceinline__ void quarter(const Slot<M, GU>& s, int d, const uint32_t* xq,
                                         float* acc) {
+  bool fresh[5] = {FIRST, FIRST, FIRST, FIRST, FIRST};
+  auto mac = [&](int i, uint32_t c, uint32_t xx) {
+    if (fresh[i]) {
+      acc[i] = dot2z(c, xx);
+      fresh[i] = false;
+    } else {
+      acc[i] = dot2(c, xx, acc[i]);
+    }
+  };
   if constexpr (M == 2) {
     // fields j = 0..4 in place (value q 2^(2j) 2^-24), 5..7 after a shift by 6
 #pragma unroll
     for (int e = 0; e < 2; e++) {
       const uint32_t w = s0_dword(s.a, s.b, 2 * d + e);
       const uint32_t* x8 = xq + 8 * e;
-      acc[0] = dot2(w & 0x00030003u, x8[0], acc[0]);
-      acc[1] = dot2(w & 0x000C000Cu, x8[1], acc[1]);
-      acc[2] = dot2(w & 0x00300030u, x8[2], acc[2]);
-      acc[3] = dot2(w & 0x00C000C0u, x8[3], acc[3]);
-      acc[4] = dot2(w & 0x03000300u, x8[4], acc[4]);
+      mac(0, w & 0x00030003u, x8[0]);
+      mac(1, w & 0x000C000Cu, x8[1]);
+      mac(2, w & 0x00300030u, x8[2]);
+      mac(3, w & 0x00C000C0u, x8[3]);
+      mac(4, w & 0x03000300u, x8[4]);
       const uint32_t t = w >> 6;
-      acc[2] = dot2(t & 0x00300030u, x8[5], acc[2]);
-      acc[3] = dot2(t & 0x00C000C0u, x8[6], acc[3]);
-      acc[4] = dot2(t & 0x03000300u, x8[7], acc[4]);
+      mac(2, t & 0x00300030u, x8[5]);
+      mac(3, t & 0x00C000C0u, x8[6]);
+      mac(4, t & 0x03000300u, x8[7]);
     }
   } else {
     uint32_t ye, yo;
@@ -170,6 +193,7 @@ __device__ __forceinline__ void quarter(const Slot<M, GU>& s, int d, const uint3
     } else {
       ye = (p3 << 1) & 0xAAAAAAAAu;
       yo = p3 & 0xAAAAAAAAu;
+      keep(ye); keep(yo);
     }
     uint32_t ve = 0, vo = 0, we = 0, wo = 0;
     if constexpr (M >= 5) {
@@ -179,6 +203,7 @@ __device__ __forceinline__ void quarter(const Slot<M, GU>& s, int d, const uint3
       } else {
         ve = (p5 << 1) & 0xAAAAAAAAu;
         vo = p5 & 0xAAAAAAAAu;
+        keep(ve); keep(vo);
       }
       if constexpr (M >= 7) {
         const uint32_t p7 = s.pl[4][d];
@@ -187,6 +212,7 @@ __device__ __forceinline__ void quarter(const Slot<M, GU>& s, int d, const uint3
         } else {
           we = (p7 << 1) & 0xAAAAAAAAu;
           wo = p7 & 0xAAAAAAAAu;
+          keep(we); keep(wo);
         }
       }
     }
@@ -200,10 +226,10 @@ __device__ __forceinline__ void quarter(const Slot<M, GU>& s, int d, const uint3
 #pragma unroll
       for (int h = 0; h < 2; h++) {
         const uint32_t zz = z[h], t = zz >> 8;
-        acc[0] = dot2(zz & 0x000F000Fu, xw[h], acc[0]);
-        acc[1] = dot2(zz & 0x00F000F0u, xw[2 + h], acc[1]);
-        acc[0] = dot2(t & 0x000F000Fu, xw[4 + h], acc[0]);
-        acc[1] = dot2(t & 0x00F000F0u, xw[6 + h], acc[1]);
+        mac(0, zz & 0x000F000Fu, xw[h]);
+        mac(1, zz & 0x00F000F0u, xw[2 + h]);
+        mac(0, t & 0x000F000Fu, xw[4 + h]);
+        mac(1, t & 0x00F000F0u, xw[6 + h]);
       }
       if constexpr (M >= 5) {
         uint32_t v[2];
@@ -211,10 +237,10 @@ __device__ __forceinline__ void quarter(const Slot<M, GU>& s, int d, const uint3
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const uint32_t zz = v[h], t = zz >> 8;
-          acc[1] = dot2(zz & 0x000F000Fu, xw[h], acc[1]);
-          acc[2] = dot2(zz & 0x00F000F0u, xw[2 + h], acc[2]);
-          acc[1] = dot2(t & 0x000F000Fu, xw[4 + h], acc[1]);
-          acc[2] = dot2(t & 0x00F000F0u, xw[6 + h], acc[2]);
+          mac(1, zz & 0x000F000Fu, xw[h]);
+          mac(2, zz & 0x00F000F0u, xw[2 + h]);
+          mac(1, t & 0x000F000Fu, xw[4 + h]);
+          mac(2, t & 0x00F000F0u, xw[6 + h]);
         }
       }
     }
@@ -222,17 +248,13 @@ __device__ __forceinline__ void quarter(const Slot<M, GU>& s, int d, const uint3
 }
 
 // sum over one tile of (s_M u_M + lo_M) x, i.e. Eq. 10 summed per group.
-// xl: the tile's 64 x pairs in LDS (wave-uniform address), read one quarter
-// ahead of use; sx: the tile's per-group sum(x).
+// xl: the tile's 64 x pairs in LDS, read one quarter ahead of use, followed
+// by the tile's per-group sum(x) (xl[64 + gi]).
 template <int M, int GU>
-__device__ __forceinline__ float tile_partial(const Slot<M, GU>& s, const uint32_t* xl, const float* sx) {
+__device__ __forceinline__ float tile_partial(const Slot<M, GU>& s, const uint32_t* xl, float part) {
   constexpr float kM = float((1 << (M - 2)) - 1) / float(1 << (M - 1));  // (2^(M-2)-1)/2^(M-1)
-  constexpr int kAcc = M == 2 ? 5 : 3;
+  constexpr int kAcc = M == 2 ? 5 : (M >= 5 ? 3 : 2);
   float acc[GU][kAcc];
-#pragma unroll
-  for (int gi = 0; gi < GU; gi++)
-#pragma unroll
-    for (int i = 0; i < kAcc; i++) acc[gi][i] = 0.f;
   const u32x4* xl4 = reinterpret_cast<const u32x4*>(xl);
   uint32_t xq[2][16];
 #pragma unroll
@@ -251,26 +273,36 @@ __device__ __forceinline__ float tile_partial(const Slot<M, GU>& s, const uint32
       }
     }
     float* a = acc[d * GU / 4];
-    quarter<M, GU>(s, d, xq[d & 1], a);
+    if (d % (4 / GU) == 0)
+      quarter<M, GU, true>(s, d, xq[d & 1], a);
+    else
+      quarter<M, GU, false>(s, d, xq[d & 1], a);
     // An empty volatile statement that takes the quarter's accumulators and
     // clobbers memory: the quarter is computed here, and the reads of quarter
     // d + 2 cannot move above it, so at most two quarters of x are live.
     if constexpr (kAcc == 5)
       asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]) :: "memory");
-    else
+    else if constexpr (kAcc == 3)
       asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]) :: "memory");
+    else
+      asm volatile("" : "+v"(a[0]), "+v"(a[1]) :: "memory");
   }
-  float part = 0.f;
+  const float* sx = reinterpret_cast<const float*>(xl + 64);
 #pragma unroll
   for (int gi = 0; gi < GU; gi++) {
     float q;
     if constexpr (M == 2)   // s_2 sum(q x): field j accumulated at scale 2^(2j-24)
       q = acc[gi][0] * 0x1p24f + acc[gi][1] * 0x1p22f + acc[gi][2] * 0x1p20f + acc[gi][3] * 0x1p18f +
           acc[gi][4] * 0x1p16f;
-    else                    // s_M sum(u_M x) = s * (A 2^22 + B 2^18 + C 2^14) for every M >= 3
-      q = acc[gi][0] * 0x1p22f + acc[gi][1] * 0x1p18f + (M >= 5 ? acc[gi][2] * 0x1p14f : 0.f);
+    else if constexpr (M >= 5)  // s_M sum(u_M x) = s * (A 2^22 + B 2^18 + C 2^14) for every M >= 3
+      q = acc[gi][0] * 0x1p22f + acc[gi][1] * 0x1p18f + acc[gi][2] * 0x1p14f;
+    else
+      q = acc[gi][0] * 0x1p22f + acc[gi][1] * 0x1p18f;
     const float lo = h2f(s.meta[gi] & 0xffffu), st = h2f(s.meta[gi] >> 16);
-    part += st * (q - kM * sx[gi]) + lo * sx[gi];
+    // s (sum u_M x) + lo_M sum(x), lo_M = lo - k_M s (Eq. 10); k_2 = 0
+    const float loM = M == 2 ? lo : __builtin_fmaf(-kM, st, lo);
+    part = __builtin_fmaf(st, q, part);
+    part = __builtin_fmaf(loM, sx[gi], part);
   }
   return part;
 }
@@ -314,7 +346,7 @@ __device__ __forceinline__ float seg_scan64(float v, int r) {
 constexpr int kEntries = 2;      // side-record entries prefetched per thread (in-workgroup mode)
 constexpr int kSideBatches = 8;  // 64-entry batches the side-record wave keeps in flight
 constexpr int kXChunks = 4;      // 16-byte x chunks staged per lane: up to 4 steps per wave
-constexpr int kXPitch = 68;      // LDS dwords per tile of x: 64 + 4 of padding
+constexpr int kXPitch = 68;      // LDS dwords per tile: 64 of x, then up to 4 group sums of x
 
 // Side-record wave (SIDE mode): the side record of one 16-row block, run by
 // the workgroup's extra wave while the others stream the main stream.
@@ -378,7 +410,6 @@ template <int M, int GU, int D, int SIDE>
 __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
   uint32_t* xs = reinterpret_cast<uint32_t*>(lds);            // x pairs, tile t at t * kXPitch
-  float* sx_s = reinterpret_cast<float*>(lds + p.lds_sx);     // sum(x) per group
   float* part_s = reinterpret_cast<float*>(lds + p.lds_part); // lane partials per wave
   int32_t* rp_s = reinterpret_cast<int32_t*>(lds + p.lds_rp); // the block's row_ptr (+ spare)
   float* runs_s = reinterpret_cast<float*>(lds + p.lds_runs); // run sums / side total per row
@@ -469,7 +500,9 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     u = row_shr_add<2>(v); v = li >= 2 ? u : v;
     if constexpr (kCpg >= 8) { u = row_shr_add<4>(v); v = li >= 4 ? u : v; }
     if constexpr (kCpg >= 16) { u = row_shr_add<8>(v); v = li >= 8 ? u : v; }
-    sx_s[ok && li == kCpg - 1 ? ci / kCpg : p.C / p.g] = v;
+    // sum(x) of group (ci & 15) / kCpg of tile ci / 16 sits after the tile's x
+    // (spare lanes write into the spare tile)
+    xs[(ok && li == kCpg - 1 ? (ci >> 4) : p.T) * kXPitch + 64 + (ci & 15) / kCpg] = __builtin_bit_cast(uint32_t, v);
   }
   if constexpr (!SIDE) rp_s[w == 0 && lane <= 16 ? lane : 17] = int32_t(rpv);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -480,14 +513,11 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   //     range -> zeros, no traffic), which keeps every wait count
   //     path-independent.
   float part = 0.f;
+  // LDS x of the lane's tile at step i: tile 4 (q0 + i) + cg, clamped to the
+  // row's last tile (lanes past the row's end have zero weights).
+  const int xo0 = (4 * q0 + cg) * kXPitch, xlast = (p.T - 1) * kXPitch;
   auto step = [&](Slot<M, GU>& s, int i) {
-    if (i < nq) {
-      const int t = min(4 * (q0 + i) + cg, p.T - 1);   // lanes past the row's end read zeros
-      float sx[GU];
-#pragma unroll
-      for (int gi = 0; gi < GU; gi++) sx[gi] = sx_s[t * GU + gi];
-      part += tile_partial<M, GU>(s, xs + t * kXPitch, sx);
-    }
+    if (i < nq) part = tile_partial<M, GU>(s, xs + min(xo0 + 4 * kXPitch * i, xlast), part);
     __builtin_amdgcn_sched_barrier(0);   // reuse the slot's registers: no loads hoisted above
     issue(s, rW, chunk, rMeta, ubase + uint32_t(i + D) * 64u, valid(i + D));
   };
@@ -653,14 +683,11 @@ static int env_int(const char* name, int dflt) {
 constexpr int kDepth[9] = {0, 0, 2, 2, 1, 1, 1, 1, 1};
 constexpr int kMaxWaves = 16;   // waves per workgroup (incl. a side-record wave): __launch_bounds__(1024)
 
-// LDS carve-up: x padded to 68 dwords per tile (plus a spare chunk), sum(x)
-// per group (plus a spare slot), per-wave lane partials, the block's row_ptr
+// LDS carve-up: per tile 64 dwords of x and its per-group sum(x) (up to 4
+// dwords; plus a spare tile), per-wave lane partials, the block's row_ptr
 // (plus a spare slot), side-record run sums (17 per 64-entry batch).
-static size_t lds_layout(int C, int g, int S, dev::GemvParams* prm) {
+static size_t lds_layout(int C, int S, dev::GemvParams* prm) {
   size_t o = size_t(C / kTileCols + 1) * dev::kXPitch * 4;
-  if (prm) prm->lds_sx = uint32_t(o);
-  o += (size_t(C / g) + 1) * 4;
-  o = (o + 15) & ~size_t(15);
   if (prm) prm->lds_part = uint32_t(o);
   o += size_t(S) * 64 * 4;
   if (prm) prm->lds_rp = uint32_t(o);
@@ -700,7 +727,7 @@ static bool plan_gemv(const ImageHeader& h, LaunchCfg* c) {
   c->side = side;
   c->grid = nblk;
   c->nt_max = (Q + S - 1) / S;
-  c->lds = lds_layout(h.cols, h.group, S, &c->prm);
+  c->lds = lds_layout(h.cols, S, &c->prm);
   if (c->lds > device_lds_limit()) return false;
   c->prm.R = h.rows; c->prm.C = h.cols; c->prm.T = T; c->prm.S = S; c->prm.g = h.group;
   return true;
