@@ -490,16 +490,20 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     const int c = lane + 64 * k;
     const bool ok = c < nch;
     const int ci = cbase + c;
-    const int xo = ok ? (ci >> 4) * kXPitch + (ci & 15) * 4 : p.T * kXPitch;
+    // (a 24-bit multiply: a 32-bit one becomes a 64-bit multiply-add whose
+    // unused high addend can land on a pending load's register and wait for it)
+    const int xo = ok ? int(__umul24(uint32_t(ci >> 4), uint32_t(kXPitch))) + (ci & 15) * 4 : p.T * kXPitch;
     *reinterpret_cast<u32x4*>(xs + xo) = xv[k];
     float v = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; i++) v = dot2(xv[k][i], kOneOne, v);
     float u;
-    u = row_shr_add<1>(v); v = li >= 1 ? u : v;
-    u = row_shr_add<2>(v); v = li >= 2 ? u : v;
-    if constexpr (kCpg >= 8) { u = row_shr_add<4>(v); v = li >= 4 ? u : v; }
-    if constexpr (kCpg >= 16) { u = row_shr_add<8>(v); v = li >= 8 ? u : v; }
+    // (a group of 16 chunks is a whole DPP row, whose edges read zeros: no
+    // masking; smaller groups mask the lanes that would read the group below)
+    u = row_shr_add<1>(v); v = kCpg == 16 || li >= 1 ? u : v;
+    u = row_shr_add<2>(v); v = kCpg == 16 || li >= 2 ? u : v;
+    if constexpr (kCpg >= 8) { u = row_shr_add<4>(v); v = kCpg == 16 || li >= 4 ? u : v; }
+    if constexpr (kCpg >= 16) { u = row_shr_add<8>(v); v = u; }
     // sum(x) of group (ci & 15) / kCpg of tile ci / 16 sits after the tile's x
     // (spare lanes write into the spare tile)
     xs[(ok && li == kCpg - 1 ? (ci >> 4) : p.T) * kXPitch + 64 + (ci & 15) / kCpg] = __builtin_bit_cast(uint32_t, v);
@@ -703,9 +707,12 @@ static size_t lds_layout(int C, int S, dev::GemvParams* prm) {
 // waves on every SIMD (8 per CU), within [ceil(groups / 4), min(16, groups)]
 // (a wave stages the x of at most 4 steps).  With at least two workgroups per
 // CU the side record goes to an extra wave (its latency then hides behind
-// other workgroups; with fewer it would sit on the critical path).
+// other workgroups; with fewer it would sit on the critical path), and below
+// 4 bits, where a step is cheapest, each wave takes the most steps it can
+// (measured on 14336 x 4096: 7.2 / 8.2 us at 2 / 3 bits against 7.6 / 8.6
+// with two waves per SIMD; at 4 bits two waves per SIMD stay ahead).
 // STAGQ_WAVES and STAGQ_SIDE override the choices (tuning).
-static bool plan_gemv(const ImageHeader& h, LaunchCfg* c) {
+static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   const int T = h.cols / kTileCols;
   const int Q = (T + 3) / 4;
   const int nblk = h.blocks;
@@ -719,6 +726,7 @@ static bool plan_gemv(const ImageHeader& h, LaunchCfg* c) {
   if (smin > smax) return false;
   const int target = 2 * 4 * cus;
   int S = (target + nblk - 1) / nblk;
+  if (side && bits <= 3) S = smin;
   S = std::max(smin, std::min(smax, S));
   const int s_env = env_int("STAGQ_WAVES", 0);
   if (s_env) S = s_env;
@@ -827,7 +835,7 @@ int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stre
   if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 4) return STAGQ_EALIGN;
   const int GU = kTileCols / H.group;
   LaunchCfg c;
-  if (!plan_gemv(H, &c)) return STAGQ_ESHAPE;
+  if (!plan_gemv(H, bits, &c)) return STAGQ_ESHAPE;
   const uint8_t* b = h->dev;
   c.prm.s0 = b + H.off_s0;
   c.prm.meta = b + H.off_meta;
@@ -861,7 +869,7 @@ int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, in
   if (!layout(rows, cols, group, nbits, 0, &H)) return STAGQ_ESHAPE;
   if (bits < 2 || bits > nbits) return STAGQ_EBITS;
   LaunchCfg c;
-  if (!plan_gemv(H, &c)) return STAGQ_ESHAPE;
+  if (!plan_gemv(H, bits, &c)) return STAGQ_ESHAPE;
   out[0] = c.grid; out[1] = 64 * (c.S + (c.side ? 1 : 0)); out[2] = c.S; out[3] = c.nt_max;
   out[4] = kBlockRows; out[5] = int32_t(c.lds); out[6] = c.side ? 1 : 0; out[7] = kDepth[bits];
   return STAGQ_OK;

@@ -150,3 +150,21 @@ def test_unsupported_shapes():
 def test_strerror_covers_every_status():
     for st in range(0, -10, -1):
         assert pwo.lib().stagq_strerror(st).decode() != "unknown status"
+
+
+def test_launch_plan_shapes():
+    """Launch shapes for a 256-CU device (the host-only default): one
+    workgroup per 16-row block; with two or more blocks per CU the side record
+    runs on an extra wave and, below 4 bits, each wave takes the most steps
+    it can (4, as x is staged for at most 4 steps)."""
+    def plan(R, Cc, bits, g=128, N=4):
+        out = (C.c_int32 * 8)()
+        assert pwo.lib().stagq_plan_gemv(R, Cc, g, N, bits, out) == 0
+        return dict(grid=out[0], threads=out[1], S=out[2], steps=out[3], side=out[6])
+    p2, p4 = plan(14336, 4096, 2), plan(14336, 4096, 4)
+    assert (p2["grid"], p2["S"], p2["steps"], p2["side"], p2["threads"]) == (896, 2, 4, 1, 192)
+    assert (p4["S"], p4["steps"], p4["threads"]) == (3, 3, 256)
+    d = plan(4096, 14336, 2)
+    assert (d["grid"], d["S"], d["side"], d["threads"]) == (256, 8, 0, 512)
+    lm = plan(128256, 4096, 3)
+    assert (lm["grid"], lm["S"], lm["side"]) == (8016, 2, 1)
