@@ -114,7 +114,7 @@ struct GemvParams {
   const uint32_t* x;       // fp16 pairs
   float* y;
   uint32_t chunk_bytes, meta_bytes, side_bytes, rp_bytes, x_bytes;
-  int32_t R, C, T, S;      // rows, cols, tiles per row, waves (column slices) per workgroup
+  int32_t R, C, T, T4, S;  // rows, cols, tiles per row (padded to a multiple of 4), waves per workgroup
   int32_t g;
   uint32_t lds_part;          // LDS offset of the lane partials (x and sum(x) at 0)
   uint32_t lds_rp, lds_runs;  // LDS offsets of the block's row_ptr and the side-record run sums
@@ -127,25 +127,31 @@ struct Slot {
   uint32_t meta[GU];                 // (lo | s << 16) of the tile's groups
 };
 
-// Loads of one tile column.  rW covers the base stream and the planes, which
-// follow each other at a stride of chunk bytes (chunk k at soffset k * chunk);
-// an out-of-range voffset reads zeros.
+// Loads of step i of a wave: the lane's tile is its step-0 tile plus 64 i.
+// rW covers the base stream and the planes, which follow each other at a
+// stride of chunk bytes; stream k and step i are a scalar offset
+// (k chunk + 1024 i) on the lane's fixed voffset vW (vM for the group pairs).
+// A step past the wave's last (ok false, wave-uniform) reads zeros: its
+// voffset is out of range.
 template <int M, int GU>
 __device__ __forceinline__ void issue(Slot<M, GU>& s, const rsrc_t& rW, uint32_t chunk,
-                                      const rsrc_t& rMeta, uint32_t tile, bool ok) {
-  const uint32_t off = ok ? tile * 16u : kOOB;
-  s.a = __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0);
-  s.b = __builtin_amdgcn_raw_buffer_load_b128(rW, off, int(chunk), 0);
+                                      const rsrc_t& rMeta, uint32_t vW, uint32_t vM, int i, bool ok) {
+  const uint32_t off = ok ? vW : kOOB;
+  const int so = i * 1024;
+  s.a = __builtin_amdgcn_raw_buffer_load_b128(rW, off, so, 0);
+  s.b = __builtin_amdgcn_raw_buffer_load_b128(rW, off, int(chunk) + so, 0);
 #pragma unroll
-  for (int k = 0; k < M - 2; k++) s.pl[k] = __builtin_amdgcn_raw_buffer_load_b128(rW, off, int((k + 2) * chunk), 0);
-  const uint32_t offm = ok ? tile * (4u * GU) : kOOB;
+  for (int k = 0; k < M - 2; k++)
+    s.pl[k] = __builtin_amdgcn_raw_buffer_load_b128(rW, off, int((k + 2) * chunk) + so, 0);
+  const uint32_t offm = ok ? vM : kOOB;
+  const int som = i * (256 * GU);
   if constexpr (GU == 1) {
-    s.meta[0] = ld32(rMeta, offm);
+    s.meta[0] = __builtin_amdgcn_raw_buffer_load_b32(rMeta, offm, som, 0);
   } else if constexpr (GU == 2) {
-    u32x2 v = ld64(rMeta, offm);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rMeta, offm, som, 0);
     s.meta[0] = v[0]; s.meta[1] = v[1];
   } else {
-    u32x4 v = ld128(rMeta, offm);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rMeta, offm, som, 0);
     s.meta[0] = v[0]; s.meta[1] = v[1]; s.meta[2] = v[2]; s.meta[3] = v[3];
   }
 }
@@ -434,11 +440,12 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   const int cg = lane >> 4;                       // tile column within the four
   const int Q = (p.T + 3) >> 2;                    // groups of four tile columns
   const int q0 = (w * Q) / p.S, nq = ((w + 1) * Q) / p.S - q0;
-  const uint32_t ubase = uint32_t(blk * p.T + 4 * q0) * 16u + uint32_t(lane);  // tile of step 0
+  const uint32_t ubase = uint32_t(blk * p.T4 + 4 * q0) * 16u + uint32_t(lane);  // tile of step 0
+  const uint32_t vW = ubase * 16u, vM = ubase * (4u * GU);
   const uint32_t chunk = p.chunk_bytes;
   const rsrc_t rW = mk(p.s0, uint32_t(M) * chunk);
   const rsrc_t rMeta = mk(p.meta, p.meta_bytes);
-  auto valid = [&](int i) { return i < nq && 4 * (q0 + i) + cg < p.T; };
+  auto valid = [&](int i) { return i < nq; };   // (tile columns past the row's end are zero tiles)
 
   // --- prologue, in arrival order: (in-workgroup mode) the block's row_ptr,
   //     the x of this wave's tile columns, then D steps of weights.
@@ -446,7 +453,9 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   if constexpr (!SIDE)
     rpv = ld32(rRp, lane <= 16 ? uint32_t(min(blk * 16 + lane, p.R)) * 4u : kOOB);
   const int cbase = 4 * q0 * 16;                         // first x chunk (8 columns) of the wave
-  const int nch = min(4 * nq * 16, (p.C >> 3) - cbase);  // x chunks of the wave
+  // x chunks of the wave's quads (those past the row's end, in its zero
+  // tiles, load as zeros)
+  const int nch = min(4 * nq * 16, p.T4 * 16 - cbase);
   u32x4 xv[kXChunks];
 #pragma unroll
   for (int k = 0; k < kXChunks; k++) {
@@ -457,7 +466,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   Slot<M, GU> sl[D];
 #pragma unroll
   for (int i = 0; i < D; i++) {
-    issue(sl[i], rW, chunk, rMeta, ubase + uint32_t(i) * 64u, valid(i));
+    issue(sl[i], rW, chunk, rMeta, vW, vM, i, valid(i));
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -492,7 +501,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     const int ci = cbase + c;
     // (a 24-bit multiply: a 32-bit one becomes a 64-bit multiply-add whose
     // unused high addend can land on a pending load's register and wait for it)
-    const int xo = ok ? int(__umul24(uint32_t(ci >> 4), uint32_t(kXPitch))) + (ci & 15) * 4 : p.T * kXPitch;
+    const int xo = ok ? int(__umul24(uint32_t(ci >> 4), uint32_t(kXPitch))) + (ci & 15) * 4 : p.T4 * kXPitch;
     *reinterpret_cast<u32x4*>(xs + xo) = xv[k];
     float v = 0.f;
 #pragma unroll
@@ -506,7 +515,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     if constexpr (kCpg >= 16) { u = row_shr_add<8>(v); v = u; }
     // sum(x) of group (ci & 15) / kCpg of tile ci / 16 sits after the tile's x
     // (spare lanes write into the spare tile)
-    xs[(ok && li == kCpg - 1 ? (ci >> 4) : p.T) * kXPitch + 64 + (ci & 15) / kCpg] = __builtin_bit_cast(uint32_t, v);
+    xs[(ok && li == kCpg - 1 ? (ci >> 4) : p.T4) * kXPitch + 64 + (ci & 15) / kCpg] = __builtin_bit_cast(uint32_t, v);
   }
   if constexpr (!SIDE) rp_s[w == 0 && lane <= 16 ? lane : 17] = int32_t(rpv);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -517,13 +526,13 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   //     range -> zeros, no traffic), which keeps every wait count
   //     path-independent.
   float part = 0.f;
-  // LDS x of the lane's tile at step i: tile 4 (q0 + i) + cg, clamped to the
-  // row's last tile (lanes past the row's end have zero weights).
-  const int xo0 = (4 * q0 + cg) * kXPitch, xlast = (p.T - 1) * kXPitch;
+  // LDS x of the lane's tile at step i: tile 4 (q0 + i) + cg (zero x past
+  // the row's end, where the weights are zero tiles too).
+  const int xo0 = (4 * q0 + cg) * kXPitch;
   auto step = [&](Slot<M, GU>& s, int i) {
-    if (i < nq) part = tile_partial<M, GU>(s, xs + min(xo0 + 4 * kXPitch * i, xlast), part);
+    if (i < nq) part = tile_partial<M, GU>(s, xs + xo0 + 4 * kXPitch * i, part);
     __builtin_amdgcn_sched_barrier(0);   // reuse the slot's registers: no loads hoisted above
-    issue(s, rW, chunk, rMeta, ubase + uint32_t(i + D) * 64u, valid(i + D));
+    issue(s, rW, chunk, rMeta, vW, vM, i + D, valid(i + D));
   };
 #pragma unroll
   for (int i = 0; i < D; i++) step(sl[i], i);
@@ -606,7 +615,7 @@ struct CodesParams {
   const uint8_t* planes;
   uint8_t* codes;
   uint32_t chunk_bytes;
-  int32_t R, T, C;
+  int32_t R, T, T4, C;
   int64_t tiles;
 };
 
@@ -614,9 +623,9 @@ template <int M>
 __global__ void __launch_bounds__(256) codes_kernel(const CodesParams p) {
   const int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (u >= p.tiles) return;
-  const int64_t row = (u / (16 * int64_t(p.T))) * 16 + (u & 15);
-  const int64_t tc = (u >> 4) % p.T;
-  if (row >= p.R) return;
+  const int64_t row = (u / (16 * int64_t(p.T4))) * 16 + (u & 15);
+  const int64_t tc = (u >> 4) % p.T4;
+  if (row >= p.R || tc >= p.T) return;   // padding rows and zero tiles
   const rsrc_t rA = mk(p.s0, p.chunk_bytes), rB = mk(p.s0 + p.chunk_bytes, p.chunk_bytes);
   const uint32_t off = uint32_t(u) * 16u;
   const u32x4 a = ld128(rA, off), b = ld128(rB, off);
@@ -687,11 +696,12 @@ static int env_int(const char* name, int dflt) {
 constexpr int kDepth[9] = {0, 0, 2, 2, 1, 1, 1, 1, 1};
 constexpr int kMaxWaves = 16;   // waves per workgroup (incl. a side-record wave): __launch_bounds__(1024)
 
-// LDS carve-up: per tile 64 dwords of x and its per-group sum(x) (up to 4
-// dwords; plus a spare tile), per-wave lane partials, the block's row_ptr
-// (plus a spare slot), side-record run sums (17 per 64-entry batch).
+// LDS carve-up: per tile (padded tile columns, plus a spare tile) 64 dwords
+// of x and its per-group sum(x) (up to 4 dwords), per-wave lane partials, the
+// block's row_ptr (plus a spare slot), side-record run sums (17 per 64-entry
+// batch).
 static size_t lds_layout(int C, int S, dev::GemvParams* prm) {
-  size_t o = size_t(C / kTileCols + 1) * dev::kXPitch * 4;
+  size_t o = size_t(padded_tcols(C) + 1) * dev::kXPitch * 4;
   if (prm) prm->lds_part = uint32_t(o);
   o += size_t(S) * 64 * 4;
   if (prm) prm->lds_rp = uint32_t(o);
@@ -737,7 +747,8 @@ static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   c->nt_max = (Q + S - 1) / S;
   c->lds = lds_layout(h.cols, S, &c->prm);
   if (c->lds > device_lds_limit()) return false;
-  c->prm.R = h.rows; c->prm.C = h.cols; c->prm.T = T; c->prm.S = S; c->prm.g = h.group;
+  c->prm.R = h.rows; c->prm.C = h.cols; c->prm.T = T; c->prm.T4 = int32_t(padded_tcols(h.cols));
+  c->prm.S = S; c->prm.g = h.group;
   return true;
 }
 
@@ -889,6 +900,7 @@ int stagq_decode_codes(stagq_handle h, int bits, uint8_t* codes, void* hip_strea
   p.chunk_bytes = uint32_t(H.bytes_s0_chunk);
   p.R = H.rows;
   p.T = H.cols / kTileCols;
+  p.T4 = int32_t(padded_tcols(H.cols));
   p.C = H.cols;
   p.tiles = H.tiles;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);

@@ -93,14 +93,14 @@ uint64_t bytes_read(const ImageHeader& h, int bits) {
 // Writes the tiles of rows [r0, r1) (all tile columns).
 static void pack_rows(const stagq_fields* f, const ImageHeader& h, uint8_t* img, int64_t r0,
                       int64_t r1) {
-  const int64_t C = f->cols, n = int64_t(f->rows) * C, T = C / kTileCols;
+  const int64_t C = f->cols, n = int64_t(f->rows) * C, T = C / kTileCols, T4 = padded_tcols(C);
   const int N = f->nbits_max, GU = kTileCols / f->group, G = C / f->group;
   uint32_t* s0a = reinterpret_cast<uint32_t*>(img + h.off_s0);
   uint32_t* s0b = reinterpret_cast<uint32_t*>(img + h.off_s0 + h.bytes_s0_chunk);
   uint32_t* meta = reinterpret_cast<uint32_t*>(img + h.off_meta);
   for (int64_t r = r0; r < r1; r++)
     for (int64_t t = 0; t < T; t++) {
-      const int64_t u = tile_index(r, t, T), c0 = t * kTileCols;
+      const int64_t u = tile_index(r, t, T4), c0 = t * kTileCols;
       const uint8_t* q = f->q + r * C + c0;
       uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int c = 0; c < kTileCols; c++) w[col_dword(c)] |= uint32_t(q[c]) << (2 * col_field(c));
@@ -213,14 +213,14 @@ int stagq_unpack_host(const void* image, size_t image_bytes, stagq_info* shape, 
   shape->nnz = h.nnz; shape->image_bytes = h.total;
   for (int b = 2; b <= h.nbits; b++) shape->bytes_read[b] = bytes_read(h, b);
   const uint8_t* img = static_cast<const uint8_t*>(image);
-  const int64_t R = h.rows, C = h.cols, T = C / kTileCols, n = R * C;
+  const int64_t R = h.rows, C = h.cols, T = C / kTileCols, T4 = padded_tcols(C), n = R * C;
   const int GU = kTileCols / h.group, G = int(C / h.group);
   const uint32_t* s0a = reinterpret_cast<const uint32_t*>(img + h.off_s0);
   const uint32_t* s0b = reinterpret_cast<const uint32_t*>(img + h.off_s0 + h.bytes_s0_chunk);
   const uint32_t* meta = reinterpret_cast<const uint32_t*>(img + h.off_meta);
   for (int64_t r = 0; r < R; r++)
     for (int64_t t = 0; t < T; t++) {
-      const int64_t u = tile_index(r, t, T), c0 = t * kTileCols;
+      const int64_t u = tile_index(r, t, T4), c0 = t * kTileCols;
       for (int c = 0; c < kTileCols; c++) {
         const int dw = col_dword(c);
         if (q) q[r * C + c0 + c] = uint8_t(((dw < 4 ? s0a : s0b)[u * 4 + (dw & 3)] >> (2 * col_field(c))) & 3);

@@ -1,10 +1,12 @@
 // Packed-image layout shared by the host packer and the gfx950 kernels.
 //
 // The unit of storage is a "tile": 128 consecutive input columns of one row.
-// Rows are taken in blocks of 16 (the last block padded with zero rows), and
+// Rows are taken in blocks of 16 (the last block padded with zero rows), the
+// tile columns of a row are padded with zero tiles to a multiple of 4, and
 // inside a block the 16 rows of one tile column sit side by side:
 //
-//   tile index u = (row_block * T + tile_col) * 16 + (row mod 16),  T = cols / 128
+//   tile index u = (row_block * T4 + tile_col) * 16 + (row mod 16),
+//   T = cols / 128,  T4 = T rounded up to a multiple of 4
 //
 // so four consecutive tile columns of a row block form 64 consecutive tiles:
 // the 64 lanes of a wave (16 rows x 4 tile columns) read them as one
@@ -45,14 +47,14 @@ constexpr int kChunkBytes = 16;
 constexpr int kBlockRows = 16;
 constexpr int kMaxCols = 32768;   // x is staged whole in LDS (64 KB)
 constexpr uint32_t kImageMagic = 0x51474153u;  // "SAGQ"
-constexpr uint32_t kImageVersion = 3;
+constexpr uint32_t kImageVersion = 4;
 constexpr int kMaxBits = 8;
 
 struct ImageHeader {           // first 256 bytes of an image
   uint32_t magic, version;
   int32_t rows, cols, group, nbits;
   int64_t nnz;
-  int64_t tiles;               // U = padded rows * cols / 128
+  int64_t tiles;               // U = padded rows * T4
   int32_t rows_padded, blocks; // rows rounded up to 16, and their 16-row blocks
   uint64_t off_s0, off_planes, off_meta, off_rowptr, off_side, off_sideval, total;
   uint64_t bytes_s0_chunk;     // U * 16
@@ -69,9 +71,13 @@ inline int col_dword(int c) { return c >> 4; }
 inline int col_field(int c) { return ((c & 15) >> 1) + 8 * (c & 1); }
 inline int col_plane_bit(int c) { return 2 * col_field(c) + (col_dword(c) & 1); }
 
-// Tile index of (row, tile column).
-inline int64_t tile_index(int64_t row, int64_t tcol, int64_t T) {
-  return ((row / kBlockRows) * T + tcol) * kBlockRows + (row % kBlockRows);
+// Tile columns per row in the image: cols / 128 rounded up to a multiple of 4
+// (four tile columns are one contiguous piece per 16-row block).
+inline int64_t padded_tcols(int64_t cols) { return ((cols / kTileCols + 3) / 4) * 4; }
+
+// Tile index of (row, tile column); T4 = padded_tcols(cols).
+inline int64_t tile_index(int64_t row, int64_t tcol, int64_t T4) {
+  return ((row / kBlockRows) * T4 + tcol) * kBlockRows + (row % kBlockRows);
 }
 
 // Fill in every size and offset of an image; returns false for an unsupported
@@ -89,7 +95,7 @@ inline bool layout(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int
   h->rows = rows; h->cols = cols; h->group = group; h->nbits = nbits; h->nnz = nnz;
   h->blocks = (rows + kBlockRows - 1) / kBlockRows;
   h->rows_padded = h->blocks * kBlockRows;
-  h->tiles = int64_t(h->rows_padded) * (cols / kTileCols);
+  h->tiles = int64_t(h->rows_padded) * padded_tcols(cols);
   h->bytes_s0_chunk = uint64_t(h->tiles) * kChunkBytes;
   h->bytes_plane = uint64_t(h->tiles) * kChunkBytes;
   h->bytes_meta = uint64_t(h->tiles) * (kTileCols / group) * 4;

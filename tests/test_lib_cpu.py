@@ -78,14 +78,15 @@ def test_pack_roundtrip_and_size():
 def test_plane_major_layout_offsets():
     """A read at precision M touches the base stream and planes 3..M only: the
     planes follow the base stream in order of k.  Streams hold the rows padded
-    to a multiple of 16, 16 bytes per 128-column tile."""
+    to a multiple of 16 and the 128-column tiles of a row padded to a multiple
+    of 4, 16 bytes per tile."""
     w, _ = synth_matrix(13, 256, "student_t", 4)
     F = oracle.encode(w, 128, 6, 0.0)
     img = pwo.pack_host(F)
     hdr = np.frombuffer(img[:256].tobytes(), dtype=np.uint64)
     off_s0, off_planes = int(hdr[6]), int(hdr[7])
     chunk, plane = int(hdr[13]), int(hdr[14])
-    assert chunk == plane == 16 * 2 * 16        # 13 rows padded to 16, 2 tiles per row
+    assert chunk == plane == 16 * 4 * 16        # 13 rows padded to 16, 2 tiles per row padded to 4
     assert off_planes - off_s0 == 2 * chunk
     # Flipping one refinement bit in the fields changes exactly one byte, in plane 5.
     F2 = oracle.Fields(**{**F.__dict__})
