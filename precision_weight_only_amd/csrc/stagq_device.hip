@@ -118,6 +118,8 @@ struct GemvParams {
   int32_t g;
   uint32_t lds_part;          // LDS offset of the lane partials (x and sum(x) at 0)
   uint32_t lds_rp, lds_runs;  // LDS offsets of the block's row_ptr and the side-record run sums
+  uint32_t lds_flag;          // LDS offset of the per-wave x-staged flags (side-record wave mode)
+  int32_t flag_spins;         // spin limit of the side-record wave's wait for them
 };
 
 template <int M, int GU>
@@ -354,26 +356,37 @@ constexpr int kSideBatches = 8;  // 64-entry batches the side-record wave keeps 
 constexpr int kXChunks = 4;      // 16-byte x chunks staged per lane: up to 4 steps per wave
 constexpr int kXPitch = 68;      // LDS dwords per tile: 64 of x, then up to 4 group sums of x
 
+// Default spin limit of the side-record wave's wait for the staged x (about
+// 60 ms); past it the wave reads x from global memory instead, which is
+// equally correct.  Every main wave raises its flag right after staging, so
+// the wait ends long before.
+constexpr int kFlagSpins = 1 << 20;
+
 // Side-record wave (SIDE mode): the side record of one 16-row block, run by
 // the workgroup's extra wave while the others stream the main stream.
-// row_ptr -> entries -> x_c are three dependent loads, and this wave issues no
-// others, so its waits never queue behind weight traffic.  The block's entries
+// row_ptr -> entries are two dependent loads, and this wave issues no others,
+// so its waits never queue behind weight traffic; x_c is read from the x the
+// main waves stage in LDS, once every main wave has raised its flag (flag_s[w]
+// = 1; all flags were cleared before the workgroup's first barrier, which this
+// wave passes right after issuing its first load).  The block's entries
 // (contiguous in CSR order) go 64 per batch, up to kSideBatches batches in
 // flight; per batch a segmented scan by row leaves each row run's sum at its
 // last lane, which adds it to the row's total in LDS (batches in order: a fixed
 // summation order).
 template <int M>
 __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int lane, int32_t* rp_s,
-                                            float* rowc_s, const rsrc_t& rRp, const rsrc_t& rSide,
-                                            const rsrc_t& rX) {
+                                            float* rowc_s, const int32_t* flag_s, const uint32_t* xs,
+                                            const rsrc_t& rRp, const rsrc_t& rSide, const rsrc_t& rX) {
   constexpr float kHalfUlp = 2.0f / float(1 << M);   // 2^(1-M)
   const uint32_t rpv = ld32(rRp, lane <= 16 ? uint32_t(min(blk * 16 + lane, p.R)) * 4u : kOOB);
+  __builtin_amdgcn_s_barrier();          // the main waves' flags are cleared
   if (lane < 16) rowc_s[lane] = 0.f;
   const int E0 = __builtin_amdgcn_readlane(int(rpv), 0), E1 = __builtin_amdgcn_readlane(int(rpv), 16);
   if (lane <= 16) rp_s[lane] = int32_t(rpv);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  bool use_lds = false;
   for (int cb = E0; cb < E1; cb += 64 * kSideBatches) {
     uint64_t ent[kSideBatches];
 #pragma unroll
@@ -381,11 +394,31 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
       const int e = cb + 64 * j + lane;
       ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
     }
+    if (cb == E0) {                      // wait once for every main wave's x
+      int spins = 0;
+      while (__builtin_amdgcn_ballot_w64(lane < p.S &&
+                                         __hip_atomic_load(flag_s + (lane < p.S ? lane : 0), __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_WORKGROUP) != 1) != 0) {
+        if (++spins > p.flag_spins) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      use_lds = spins <= p.flag_spins;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    }
+    const uint16_t* xh = reinterpret_cast<const uint16_t*>(xs);
     uint32_t xc[kSideBatches];
+    if (use_lds) {
 #pragma unroll
-    for (int j = 0; j < kSideBatches; j++) {
-      const int e = cb + 64 * j + lane;
-      xc[j] = ld16(rX, e < E1 ? uint32_t(ent[j] >> 48) * 2u : kOOB);
+      for (int j = 0; j < kSideBatches; j++) {
+        const int c = cb + 64 * j + lane < E1 ? int(ent[j] >> 48) : 0;
+        xc[j] = xh[(c >> 7) * (2 * kXPitch) + (c & 127)];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSideBatches; j++) {
+        const int e = cb + 64 * j + lane;
+        xc[j] = ld16(rX, e < E1 ? uint32_t(ent[j] >> 48) * 2u : kOOB);
+      }
     }
 #pragma unroll
     for (int j = 0; j < kSideBatches; j++) {
@@ -419,6 +452,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   float* part_s = reinterpret_cast<float*>(lds + p.lds_part); // lane partials per wave
   int32_t* rp_s = reinterpret_cast<int32_t*>(lds + p.lds_rp); // the block's row_ptr (+ spare)
   float* runs_s = reinterpret_cast<float*>(lds + p.lds_runs); // run sums / side total per row
+  int32_t* flag_s = reinterpret_cast<int32_t*>(lds + p.lds_flag); // per main wave: x staged (SIDE)
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -431,7 +465,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
 
   if constexpr (SIDE) {
     if (w == p.S) {                      // the side-record wave
-      side_record<M>(p, blk, lane, rp_s, runs_s, rRp, rSide, rX);
+      side_record<M>(p, blk, lane, rp_s, runs_s, flag_s, xs, rRp, rSide, rX);
       __syncthreads();
       return;
     }
@@ -468,6 +502,11 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   for (int i = 0; i < D; i++) {
     issue(sl[i], rW, chunk, rMeta, vW, vM, i, valid(i));
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (SIDE) {                  // this wave's x-staged flag is cleared for the side wave
+    flag_s[w] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
   }
 
   // --- (in-workgroup mode) the thread's first side-record entries of the
@@ -521,6 +560,10 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if constexpr (SIDE) {                  // x of this wave's columns is in LDS
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __hip_atomic_store(flag_s + w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
 
   // --- main loop; the slot of step i is reloaded with step i + D (out of
   //     range -> zeros, no traffic), which keeps every wait count
@@ -699,7 +742,7 @@ constexpr int kMaxWaves = 16;   // waves per workgroup (incl. a side-record wave
 // LDS carve-up: per tile (padded tile columns, plus a spare tile) 64 dwords
 // of x and its per-group sum(x) (up to 4 dwords), per-wave lane partials, the
 // block's row_ptr (plus a spare slot), side-record run sums (17 per 64-entry
-// batch).
+// batch), per-wave x-staged flags.
 static size_t lds_layout(int C, int S, dev::GemvParams* prm) {
   size_t o = size_t(padded_tcols(C) + 1) * dev::kXPitch * 4;
   if (prm) prm->lds_part = uint32_t(o);
@@ -709,6 +752,8 @@ static size_t lds_layout(int C, int S, dev::GemvParams* prm) {
   o = (o + 15) & ~size_t(15);
   if (prm) prm->lds_runs = uint32_t(o);
   o += size_t(dev::kEntries) * S * 17 * 4;
+  if (prm) prm->lds_flag = uint32_t(o);
+  o += size_t(kMaxWaves) * 4;
   return o;
 }
 
@@ -721,7 +766,8 @@ static size_t lds_layout(int C, int S, dev::GemvParams* prm) {
 // 4 bits, where a step is cheapest, each wave takes the most steps it can
 // (measured on 14336 x 4096: 7.2 / 8.2 us at 2 / 3 bits against 7.6 / 8.6
 // with two waves per SIMD; at 4 bits two waves per SIMD stay ahead).
-// STAGQ_WAVES and STAGQ_SIDE override the choices (tuning).
+// STAGQ_WAVES and STAGQ_SIDE override the choices (tuning); STAGQ_FLAG_SPINS
+// sets the side-record wave's spin limit (testing its global-x fallback).
 static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   const int T = h.cols / kTileCols;
   const int Q = (T + 3) / 4;
@@ -738,6 +784,7 @@ static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   int S = (target + nblk - 1) / nblk;
   if (side && bits <= 3) S = smin;
   S = std::max(smin, std::min(smax, S));
+  c->prm.flag_spins = env_int("STAGQ_FLAG_SPINS", dev::kFlagSpins);
   const int s_env = env_int("STAGQ_WAVES", 0);
   if (s_env) S = s_env;
   if (S < smin || S > smax) return false;

@@ -247,6 +247,22 @@ def test_error_codes(pwo):
     assert e.value.status == -2
 
 
+def test_side_wave_reads_x_from_lds_or_global(pwo, monkeypatch):
+    """The side-record wave reads x_c from the x the main waves staged in LDS
+    once their flags are up, and from global memory when its spin limit runs
+    out first: a spin limit of 0 sends some workgroups down each road, and y
+    must be bitwise the same (same x values, same summation order)."""
+    monkeypatch.setenv("STAGQ_SIDE", "1")
+    w, xe = synth_matrix(2048, 1024, "student_t", 11)
+    F = oracle.encode(w, 128, 4, 0.02)
+    m, xd = _check(pwo, F, xe, (2, 4), "side wave x source (default spins)")
+    ys = {M: m.gemv(xd, M).cpu().numpy() for M in (2, 4)}
+    monkeypatch.setenv("STAGQ_FLAG_SPINS", "0")
+    for M in (2, 4):
+        _say("side wave x source (spin limit 0)", f"bits={M}")
+        assert np.array_equal(m.gemv(xd, M).cpu().numpy(), ys[M])
+
+
 @pytest.mark.parametrize("side", ["0", "1"])
 def test_side_record_modes(pwo, side, monkeypatch):
     """Both places the side record can be applied (all waves after the main
