@@ -131,7 +131,7 @@ def sweep(args):
             del w
             base = pwo.StagQMatrix.pack(fields, device=dev)
             del fields
-            n_copies = max(2, -(-args.rot_mb * (1 << 20) // base.image_bytes))
+            n_copies = max(2, -(-args.rot_mb * (1 << 20) // base.bytes_read[min(wl.bits)]))
             copies = [base] + [base.replicate() for _ in range(n_copies - 1)]
             xd = torch.from_numpy(x.view(np.int16)).view(torch.float16).to(dev)
             ys = [torch.empty(mat.rows, dtype=torch.float32, device=dev) for _ in range(n_copies)]
@@ -169,8 +169,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
-    ap.add_argument("--rot-mb", type=int, default=768, help="total size of the rotated image copies")
+    ap.add_argument("--mode", choices=("graph", "stream", "eager"), default="graph",
+                    help="graph: K launches per precision captured in one HIP graph; stream: the "
+                         "same K launches issued back to back with one event pair around them; "
+                         "eager: an event pair around every launch")
+    ap.add_argument("--rot-mb", type=int, default=1024,
+                    help="bytes (MB) the rotated image copies hold at the lowest precision read: "
+                         "every precision cycles through all copies, so at least this much is "
+                         "streamed between two reads of one copy (4x the 256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time every matrix of every workload instead of the headline line")
@@ -202,8 +208,9 @@ def main():
     K = int(np.floor(wl.frac * R * Cc + 0.5))
     fields = pwo.encode(w, wl.group, wl.nbits, K, wl.ratio_T)
     base = pwo.StagQMatrix.pack(fields, device=dev)
-    n_copies = max(6, -(-args.rot_mb * (1 << 20) // base.image_bytes))
-    n_copies += (-n_copies) % 3
+    # Enough copies that the lowest precision's reads of all of them exceed
+    # the rotation size, and every precision cycles through all of them.
+    n_copies = max(6, -(-args.rot_mb * (1 << 20) // base.bytes_read[min(bits)]))
     copies = [base] + [base.replicate() for _ in range(n_copies - 1)]
     xd = torch.from_numpy(x.view(np.int16)).view(torch.float16).to(dev)
     ys = [torch.empty(R, dtype=torch.float32, device=dev) for _ in range(n_copies)]
@@ -230,7 +237,8 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    order = {M: [3 * s + j for s in range(K)] for j, M in enumerate(bits)}   # launch ids per precision
+    # launch ids per precision: each precision cycles through every copy
+    order = {M: [j * K + s for s in range(K)] for j, M in enumerate(bits)}
     dur = {M: [] for M in bits}
 
     if args.mode == "graph":
@@ -257,6 +265,20 @@ def main():
         wall = time.perf_counter() - t_start
         for j, M in enumerate(bits):
             dur[M] = [evs[j].elapsed_time(evs[j + 1]) * 1e3 / K] * K     # microseconds per launch
+    elif args.mode == "stream":
+        # The K launches of a precision issued back to back, events around them.
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(bits) + 1)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        evs[0].record()
+        for j, M in enumerate(bits):
+            for i in order[M]:
+                launch(i, M)
+            evs[j + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        for j, M in enumerate(bits):
+            dur[M] = [evs[j].elapsed_time(evs[j + 1]) * 1e3 / K] * K
     else:
         # Eager launches with a timing event pair around every launch.
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -265,7 +287,7 @@ def main():
         t_start = time.perf_counter()
         for s in range(K):
             for j, M in enumerate(bits):
-                i = 3 * s + j
+                i = order[M][s]
                 ev[i][0].record()
                 launch(i, M)
                 ev[i][1].record()
