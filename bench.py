@@ -112,6 +112,33 @@ def graph_time(launch, n_copies, K, bits_seq):
     return e0.elapsed_time(e1) * 1e3 / K
 
 
+def read_ceiling(bytes_alg, args):
+    """Streaming-read ceiling per precision: a plain read of the same byte
+    count (stagq_stream_read), K launches in one graph cycling through fresh
+    windows of a pool larger than --rot-mb, timed like the GEMV."""
+    import torch
+    import precision_weight_only_amd as pwo
+    out = {}
+    pool_bytes = (max(args.rot_mb, 256) << 20) + (max(bytes_alg.values()) + 4096)
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for M, b in bytes_alg.items():
+        win = (b + 4095) // 4096 * 4096
+        nwin = max(2, (pool_bytes - 4096) // win)
+
+        def launch(i, _M, b=b, win=win, nwin=nwin):
+            pwo.stream_read(pool, (i % nwin) * win, b, sink)
+
+        for i in range(args.warmup):
+            launch(i, M)
+        torch.cuda.synchronize()
+        us = graph_time(launch, nwin, args.steps, [M])
+        out[M] = {"us": round(us, 3), "bytes": int(b), "gbps": round(b / us / 1e3, 1),
+                  "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2)}
+    del pool
+    return out
+
+
 def sweep(args):
     """Every matrix of the attention, MLP, Phi-4 and layer-sweep workloads at each
     precision (one graph of K launches per precision, rotating image copies),
@@ -297,6 +324,7 @@ def main():
             dur[M] = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in order[M]]
 
     bytes_alg = {M: base.bytes_read[M] for M in bits}
+    ceiling = read_ceiling(bytes_alg, args) if args.mode == "graph" else {}
     per_bits = {}
     for M in bits:
         d = np.array(dur[M])
@@ -308,6 +336,7 @@ def main():
             "gbps": round(bytes_alg[M] / (mean * 1e-6) / 1e9, 1),
             "pct_peak": round(100.0 * bytes_alg[M] / (mean * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
             "a100_stagq_us": A100_STAGQ_US[M],
+            "read_ceiling": ceiling.get(M),
             "launch": pwo.plan_gemv(R, Cc, wl.group, wl.nbits, M),
         }
     step_bytes = sum(bytes_alg.values())
@@ -323,7 +352,8 @@ def main():
         "kernel": f"gemv_kernel<M={dom}> (bits={dom})",
         "by_bits": {str(M): {"achieved": per_bits[str(M)]["gbps"],
                              "frac": round(per_bits[str(M)]["gbps"] / PEAK_HBM_GBS, 4),
-                             "traffic": (traffic or {}).get(M)} for M in bits},
+                             "traffic": (traffic or {}).get(M),
+                             "read_ceiling_gbps": (ceiling.get(M) or {}).get("gbps")} for M in bits},
     }
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

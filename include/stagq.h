@@ -155,6 +155,19 @@ int stagq_decode_codes(stagq_handle h, int bits, uint8_t* codes, void* hip_strea
 int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int bits,
                     int32_t* out);
 
+/*
+ * Streaming-read ceiling (measurement aid, not part of the method): read bytes
+ * of device memory at buf once, 16-byte loads, 16 KB per 256-thread
+ * workgroup, and discard them (sink, device uint32 [1], is written only when
+ * a checksum of the data hits one 32-bit value, which keeps the loads alive).  Timing this on
+ * the byte count a GEMV moves gives the plain-read time of those bytes on this
+ * GPU.  buf 16-byte aligned, bytes < 2^31; bytes == 0 does nothing.  One
+ * launch on hip_stream, asynchronous.  STAGQ_EINVAL for NULL pointers or
+ * bytes >= 2^31, STAGQ_EALIGN for a misaligned buf, STAGQ_EHIP on a launch
+ * error.
+ */
+int stagq_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream);
+
 /* Fill *out with shape and per-precision traffic of h. */
 int stagq_query(stagq_handle h, stagq_info* out);
 

@@ -70,6 +70,16 @@ def plan_gemv(rows: int, cols: int, group: int, nbits: int, bits: int) -> Dict[s
     return dict(zip(keys, list(out)))
 
 
+def stream_read(buf, offset: int, nbytes: int, sink, stream=None) -> None:
+    """Plain read of nbytes of the uint8 CUDA tensor buf from offset (a
+    multiple of 16): the streaming-read ceiling the GEMV is compared with.
+    sink: int32 CUDA tensor of one element."""
+    if offset % 16 or offset + nbytes > buf.numel():
+        raise ValueError("stream_read: offset must be a multiple of 16 and the window inside buf")
+    check(lib().stagq_stream_read(C.c_void_p(buf.data_ptr() + offset), int(nbytes),
+                                  C.c_void_p(sink.data_ptr()), _stream_ptr(stream)), "stagq_stream_read")
+
+
 def packed_bytes(fields) -> int:
     keep: list = []
     return int(lib().stagq_packed_bytes(C.byref(fields_struct(fields, keep))))

@@ -62,6 +62,7 @@ def _load() -> C.CDLL:
                                    C.c_double, P, P, P, P, P, P, P, C.POINTER(C.c_int64)]),
         "stagq_unpack_host": (C.c_int, [P, C.c_size_t, C.POINTER(Info), P, P, P, P, P, P, P]),
         "stagq_plan_gemv": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int, P]),
+        "stagq_stream_read": (C.c_int, [P, C.c_size_t, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -76,7 +77,7 @@ _lib = None
 EXPORTED = (
     "stagq_packed_bytes", "stagq_pack_host", "stagq_pack", "stagq_rebind", "stagq_gemv",
     "stagq_decode_codes", "stagq_query", "stagq_destroy", "stagq_strerror", "stagq_encode",
-    "stagq_unpack_host", "stagq_plan_gemv",
+    "stagq_unpack_host", "stagq_plan_gemv", "stagq_stream_read",
 )
 
 

@@ -276,3 +276,15 @@ def test_side_record_modes(pwo, side, monkeypatch):
         R, Cc, g, N, frac, dist, seed = case
         w, xe = synth_matrix(R, Cc, dist, seed)
         _check(pwo, oracle.encode(w, g, N, frac), xe, range(2, N + 1), f"edge{case} side={side}")
+
+
+def test_stream_read_ceiling_kernel(pwo):
+    """The streaming-read ceiling reads and discards: zeros never hit the
+    checksum, so sink stays untouched; a ragged byte count is fine."""
+    import torch
+    _say("stream_read 1 MiB + 48 B of zeros")
+    buf = torch.zeros((1 << 20) + 4096, dtype=torch.uint8, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    pwo.stream_read(buf, 16, (1 << 20) + 48, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7

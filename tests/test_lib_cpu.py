@@ -169,3 +169,15 @@ def test_launch_plan_shapes():
     assert (d["grid"], d["S"], d["side"], d["threads"]) == (256, 8, 0, 512)
     lm = plan(128256, 4096, 3)
     assert (lm["grid"], lm["S"], lm["side"]) == (8016, 2, 1)
+
+
+def test_stream_read_argument_errors():
+    """The streaming-read ceiling validates its arguments on the host before
+    any launch (no GPU needed for these)."""
+    lib = pwo.lib()
+    sink = C.c_void_p(64)
+    assert lib.stagq_stream_read(None, 4096, sink, None) == -1           # EINVAL
+    assert lib.stagq_stream_read(C.c_void_p(4096), 4096, None, None) == -1
+    assert lib.stagq_stream_read(C.c_void_p(4096), 1 << 31, sink, None) == -1
+    assert lib.stagq_stream_read(C.c_void_p(4104), 4096, sink, None) == -5  # EALIGN
+    assert lib.stagq_stream_read(C.c_void_p(4096), 0, sink, None) == 0       # nothing to read
