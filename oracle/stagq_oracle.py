@@ -22,6 +22,10 @@ w_main()      the additive reconstruction of Eq. (9) (the direct form; the GPU
 w_hat()       the complete reconstruction of Eq. (4): main stream outside the
               side record, the recorded value inside it.
 gemv()        y = W_hat^(M) x in float64.
+scale_x()     the activation a decoder feeds the GEMV when it applies the
+              inverse AWQ scale at run time (section 3.6, Appendix E: the
+              quantizer works on W diag(a), so x is divided by a per input
+              channel), and gemv_scaled() = gemv(scale_x(x)).
 
 Readings of the paper (where it is silent or leaves a choice open)
 ------------------------------------------------------------------
@@ -48,6 +52,9 @@ R5  Held-out entries keep the base code of their original value and all-zero
 R6  The side record stores the held-out weight itself as fp16.  For fp16
     weights this equals both of the paper's definitions of P (section 3).
 R7  A group whose stored step is 0 gets q = 0 and all-zero planes.
+R8  The run-time inverse scale arrives as one fp16 factor per input channel
+    (1 / a_c), and the scaled activation is the fp16 rounding (nearest, ties to
+    even) of the exact product x_c * (1 / a_c): the GEMV's activations are fp16.
 
 Parity status of every function is recorded next to it ("pinned by ...").
 """
@@ -60,7 +67,7 @@ import numpy as np
 
 __all__ = [
     "Fields", "encode", "quantize_value", "codes", "w_main", "w_hat", "gemv",
-    "half_step", "affine_pair", "budget",
+    "half_step", "affine_pair", "budget", "scale_x", "gemv_scaled",
 ]
 
 
@@ -287,3 +294,24 @@ def gemv(F: Fields, x16: np.ndarray, M: int, block_rows: int = 8192) -> np.ndarr
         r1 = min(F.rows, r0 + block_rows)
         y[r0:r1] = w_hat(F, M, slice(r0, r1)) @ x
     return y
+
+
+# ---------------------------------------------------------------------------
+# Run-time inverse AWQ scale (section 3.6 and Appendix E; reading R8).
+# Pinned by: unit scale gives x back, power-of-two scales scale y exactly, a
+# single scaled channel changes y by that column alone, and round-to-nearest
+# on hand-picked fp16 products.
+# ---------------------------------------------------------------------------
+def scale_x(x16: np.ndarray, inv_scale16: np.ndarray) -> np.ndarray:
+    """x'_c = fp16(x_c * inv_scale_c): the float64 product of two fp16 numbers
+    is exact, so casting it to fp16 rounds once, to nearest even."""
+    x = np.asarray(x16, dtype=np.float16).astype(np.float64)
+    a = np.asarray(inv_scale16, dtype=np.float16).astype(np.float64)
+    if x.shape != a.shape:
+        raise ValueError("x and the scale must have the same shape")
+    return (x * a).astype(np.float16)
+
+
+def gemv_scaled(F: Fields, x16: np.ndarray, inv_scale16: np.ndarray, M: int) -> np.ndarray:
+    """y = W_hat^(M) fp16(x * inv_scale) in float64."""
+    return gemv(F, scale_x(x16, inv_scale16), M)

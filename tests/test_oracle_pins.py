@@ -319,3 +319,34 @@ def test_uniform_control_centroids_sit_at_cell_midpoints():
             d = p.mean()
             tol = max(0.0008, 5 * 0.2887 / np.sqrt(p.size))
             assert abs(d - 0.5) <= tol, (M, code, d, p.size)
+
+
+def test_scale_x_rounds_the_exact_product_to_nearest_even():
+    """Reading R8 on hand-worked fp16 products: (1 + 2^-10)^2 = 1 + 2^-9 + 2^-20
+    rounds down to 1 + 2^-9; (1 + 2^-10) * 1.5 = 1.5 + 1.5 * 2^-10 is a tie
+    between 1.5 + 2^-10 (odd) and 1.5 + 2^-9 (even); 2^-14 * 0.5 is the exact
+    subnormal 2^-15; 65504 * 2 overflows to +inf; -3 * 0.25 = -0.75."""
+    x = np.array([1 + 2 ** -10, 1 + 2 ** -10, 2 ** -14, 65504.0, -3.0], dtype=np.float16)
+    a = np.array([1 + 2 ** -10, 1.5, 0.5, 2.0, 0.25], dtype=np.float16)
+    want = [1.001953125, 1.501953125, 2.0 ** -15, np.inf, -0.75]
+    with np.errstate(over="ignore"):
+        got = oracle.scale_x(x, a)
+    assert got.dtype == np.float16
+    assert [float(v) for v in got] == want
+
+
+def test_gemv_scaled_special_cases(tiny_fields):
+    """Unit scale gives the plain GEMV bitwise; a uniform factor 2 scales y by
+    exactly 2; one channel scaled by 3 changes y by that column of W_hat times
+    the change of that one activation (so the scale acts on input channels)."""
+    F, _, x = tiny_fields
+    for M in (2, 4):
+        y = oracle.gemv(F, x, M)
+        assert np.array_equal(oracle.gemv_scaled(F, x, np.ones(F.cols, np.float16), M), y)
+        assert np.array_equal(oracle.gemv_scaled(F, x, np.full(F.cols, 2.0, np.float16), M), 2.0 * y)
+        c = 37
+        a = np.ones(F.cols, np.float16)
+        a[c] = 3.0
+        dx = float(np.float16(3.0 * float(x[c]))) - float(x[c])
+        col = oracle.w_hat(F, M)[:, c]
+        assert np.allclose(oracle.gemv_scaled(F, x, a, M) - y, col * dx, rtol=1e-12, atol=1e-12)
