@@ -135,6 +135,20 @@ int stagq_rebind(stagq_handle h, void* dev_buf, size_t dev_bytes, stagq_handle* 
 int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stream);
 
 /*
+ * The GEMV with the inverse activation-aware (AWQ) scale applied to x at run
+ * time ([StagQ] section 3.6 and Appendix E: the quantizer worked on W diag(a),
+ * so the decoder multiplies input channel c by 1 / a_c where no preceding
+ * normalization absorbs it):  y = W_hat^(bits) x',  x'_c = fp16(x_c * x_scale_c),
+ * each product rounded once to fp16 (nearest even) as x is staged.
+ *   x_scale  device, fp16 [cols], 16-byte aligned: the factors 1 / a_c
+ * Everything else as stagq_gemv (same launch, same cost but one more 2-byte
+ * read per column); STAGQ_EINVAL for a NULL x_scale, STAGQ_EALIGN for a
+ * misaligned one.
+ */
+int stagq_gemv_scaled(stagq_handle h, const void* x, const void* x_scale, float* y, int bits,
+                      void* hip_stream);
+
+/*
  * Write the composite integers u_bits (Eq. 8) of the main stream as decoded by
  * the GEMV path: codes is device uint8 [rows*cols], row-major, 16-byte aligned.
  * Asynchronous on hip_stream.  (Held-out positions decode like any other: q

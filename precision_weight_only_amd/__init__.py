@@ -163,13 +163,20 @@ class StagQMatrix:
         buf.copy_(self.buffer)
         return self.clone_to(buf)
 
-    def gemv(self, x, bits: int, y=None, stream=None):
-        """y = W_hat^(bits) x for an fp16 device vector x; returns fp32 y."""
+    def gemv(self, x, bits: int, y=None, stream=None, x_scale=None):
+        """y = W_hat^(bits) x for an fp16 device vector x; returns fp32 y.
+        x_scale: optional fp16 device vector [cols] of inverse AWQ scales, applied
+        to x as it is staged (stagq_gemv_scaled)."""
         torch = _torch()
         if y is None:
             y = torch.empty(self.rows, dtype=torch.float32, device=x.device)
-        check(lib().stagq_gemv(self._h, C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()),
-                               int(bits), _stream_ptr(stream)), "stagq_gemv")
+        if x_scale is None:
+            check(lib().stagq_gemv(self._h, C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()),
+                                   int(bits), _stream_ptr(stream)), "stagq_gemv")
+        else:
+            check(lib().stagq_gemv_scaled(self._h, C.c_void_p(x.data_ptr()), C.c_void_p(x_scale.data_ptr()),
+                                          C.c_void_p(y.data_ptr()), int(bits), _stream_ptr(stream)),
+                  "stagq_gemv_scaled")
         return y
 
     def gemv_raw(self, x_ptr: int, y_ptr: int, bits: int, stream_ptr) -> int:

@@ -54,6 +54,7 @@ def _load() -> C.CDLL:
         "stagq_pack": (C.c_int, [C.POINTER(Fields), P, C.c_size_t, P, C.POINTER(P)]),
         "stagq_rebind": (C.c_int, [P, P, C.c_size_t, C.POINTER(P)]),
         "stagq_gemv": (C.c_int, [P, P, P, C.c_int, P]),
+        "stagq_gemv_scaled": (C.c_int, [P, P, P, P, C.c_int, P]),
         "stagq_decode_codes": (C.c_int, [P, C.c_int, P, P]),
         "stagq_query": (C.c_int, [P, C.POINTER(Info)]),
         "stagq_destroy": (None, [P]),
@@ -77,7 +78,7 @@ _lib = None
 EXPORTED = (
     "stagq_packed_bytes", "stagq_pack_host", "stagq_pack", "stagq_rebind", "stagq_gemv",
     "stagq_decode_codes", "stagq_query", "stagq_destroy", "stagq_strerror", "stagq_encode",
-    "stagq_unpack_host", "stagq_plan_gemv", "stagq_stream_read",
+    "stagq_unpack_host", "stagq_plan_gemv", "stagq_stream_read", "stagq_gemv_scaled",
 )
 
 

@@ -85,6 +85,10 @@ __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t b) {
 // compiler distributes the masks applied later into the inserts that built
 // the word, which costs more instructions than the insert it saves.
 __device__ __forceinline__ void keep(uint32_t& v) { asm("" : "+v"(v)); }
+// Two fp16 products, each rounded once to fp16 (nearest even).
+__device__ __forceinline__ uint32_t hmul2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, a) * __builtin_bit_cast(h2_t, b));
+}
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
@@ -115,6 +119,7 @@ struct GemvParams {
   const uint8_t* row_ptr;
   const uint8_t* side;     // side record, one u64 per entry
   const uint32_t* x;       // fp16 pairs
+  const uint32_t* xsc;     // fp16 pairs: inverse AWQ scale per input channel (scaled GEMV only)
   float* y;
   uint32_t chunk_bytes, meta_bytes, side_bytes, rp_bytes, x_bytes;
   int32_t R, C, T, T4, S;  // rows, cols, tiles per row (padded to a multiple of 4), waves per workgroup
@@ -376,7 +381,7 @@ constexpr int kFlagSpins = 1 << 20;
 // flight; per batch a segmented scan by row leaves each row run's sum at its
 // last lane, which adds it to the row's total in LDS (batches in order: a fixed
 // summation order).
-template <int M>
+template <int M, bool SC>
 __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int lane, int32_t* rp_s,
                                             float* rowc_s, const int32_t* flag_s, const uint32_t* xs,
                                             const rsrc_t& rRp, const rsrc_t& rSide, const rsrc_t& rX) {
@@ -422,6 +427,14 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
         const int e = cb + 64 * j + lane;
         xc[j] = ld16(rX, e < E1 ? uint32_t(ent[j] >> 48) * 2u : kOOB);
       }
+      if constexpr (SC) {                // the staged x is scaled: scale these the same way
+        const rsrc_t rS = mk(p.xsc, p.x_bytes);
+#pragma unroll
+        for (int j = 0; j < kSideBatches; j++) {
+          const int e = cb + 64 * j + lane;
+          xc[j] = hmul2(xc[j], ld16(rS, e < E1 ? uint32_t(ent[j] >> 48) * 2u : kOOB)) & 0xffffu;
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < kSideBatches; j++) {
@@ -447,8 +460,9 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
 // The GEMV.  SIDE selects where the side record is applied: by an extra wave
 // of the workgroup (SIDE = 1, for grids with several workgroups per CU, where
 // its latency hides behind other workgroups) or by all waves after the main
-// loop (SIDE = 0).
-template <int M, int GU, int D, int SIDE>
+// loop (SIDE = 0).  SC: x is multiplied by the per-channel inverse AWQ scale
+// p.xsc as it is staged (each product rounded once to fp16).
+template <int M, int GU, int D, int SIDE, bool SC>
 __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
   uint32_t* xs = reinterpret_cast<uint32_t*>(lds);            // x pairs, tile t at t * kXPitch
@@ -468,7 +482,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
 
   if constexpr (SIDE) {
     if (w == p.S) {                      // the side-record wave
-      side_record<M>(p, blk, lane, rp_s, runs_s, flag_s, xs, rRp, rSide, rX);
+      side_record<M, SC>(p, blk, lane, rp_s, runs_s, flag_s, xs, rRp, rSide, rX);
       __syncthreads();
       return;
     }
@@ -494,11 +508,19 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   // x chunks of the wave's quads (those past the row's end, in its zero
   // tiles, load as zeros)
   const int nch = min(4 * nq * 16, p.T4 * 16 - cbase);
-  u32x4 xv[kXChunks];
+  u32x4 xv[kXChunks], av[SC ? kXChunks : 1];
 #pragma unroll
   for (int k = 0; k < kXChunks; k++) {
     const int c = lane + 64 * k;
     xv[k] = ld128(rX, c < nch ? uint32_t(cbase + c) * 16u : kOOB);
+  }
+  if constexpr (SC) {
+    const rsrc_t rS = mk(p.xsc, p.x_bytes);
+#pragma unroll
+    for (int k = 0; k < kXChunks; k++) {
+      const int c = lane + 64 * k;
+      av[k] = ld128(rS, c < nch ? uint32_t(cbase + c) * 16u : kOOB);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   Slot<M, GU> sl[D];
@@ -542,6 +564,10 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     // (a 24-bit multiply: a 32-bit one becomes a 64-bit multiply-add whose
     // unused high addend can land on a pending load's register and wait for it)
     const int xo = ok ? int(__umul24(uint32_t(ci >> 4), uint32_t(kXPitch))) + (ci & 15) * 4 : p.T4 * kXPitch;
+    if constexpr (SC) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) xv[k][i] = hmul2(xv[k][i], av[k][i]);
+    }
     *reinterpret_cast<u32x4*>(xs + xo) = xv[k];
     float v = 0.f;
 #pragma unroll
@@ -827,10 +853,15 @@ static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
 
 template <int M, int GU, int D>
 static hipError_t launch_gemv(const LaunchCfg& c, hipStream_t st) {
-  if (c.side)
-    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 1>), dim3(c.grid), dim3(64 * (c.S + 1)), c.lds, st, c.prm);
+  const bool sc = c.prm.xsc != nullptr;
+  if (c.side && sc)
+    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 1, true>), dim3(c.grid), dim3(64 * (c.S + 1)), c.lds, st, c.prm);
+  else if (c.side)
+    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 1, false>), dim3(c.grid), dim3(64 * (c.S + 1)), c.lds, st, c.prm);
+  else if (sc)
+    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 0, true>), dim3(c.grid), dim3(64 * c.S), c.lds, st, c.prm);
   else
-    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 0>), dim3(c.grid), dim3(64 * c.S), c.lds, st, c.prm);
+    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 0, false>), dim3(c.grid), dim3(64 * c.S), c.lds, st, c.prm);
   return hipGetLastError();
 }
 
@@ -910,13 +941,16 @@ int stagq_query(stagq_handle h, stagq_info* out) {
 
 void stagq_destroy(stagq_handle h) { delete h; }
 
-int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stream) {
+static int gemv_call(stagq_handle h, const void* x, const void* x_scale, bool scaled, float* y, int bits,
+                     void* hip_stream) {
   if (!h) return STAGQ_EINVAL;
   const ImageHeader& H = h->hdr;
   if (bits < 2 || bits > H.nbits) return STAGQ_EBITS;
   if (H.rows == 0) return STAGQ_OK;  // nothing to compute; y may be empty
-  if (!x || !y) return STAGQ_EINVAL;
-  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 4) return STAGQ_EALIGN;
+  if (!x || !y || (scaled && !x_scale)) return STAGQ_EINVAL;
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 4 ||
+      reinterpret_cast<uintptr_t>(x_scale) % 16)
+    return STAGQ_EALIGN;
   const int GU = kTileCols / H.group;
   LaunchCfg c;
   if (!plan_gemv(H, bits, &c)) return STAGQ_ESHAPE;
@@ -926,6 +960,7 @@ int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stre
   c.prm.row_ptr = b + H.off_rowptr;
   c.prm.side = b + H.off_side;
   c.prm.x = static_cast<const uint32_t*>(x);
+  c.prm.xsc = scaled ? static_cast<const uint32_t*>(x_scale) : nullptr;
   c.prm.y = y;
   c.prm.chunk_bytes = uint32_t(H.bytes_s0_chunk);
   c.prm.meta_bytes = uint32_t(H.bytes_meta);
@@ -944,6 +979,15 @@ int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stre
     default: err = launch_gemv_m<8>(GU, c, st); break;
   }
   return err == hipSuccess ? STAGQ_OK : STAGQ_EHIP;
+}
+
+int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stream) {
+  return gemv_call(h, x, nullptr, false, y, bits, hip_stream);
+}
+
+int stagq_gemv_scaled(stagq_handle h, const void* x, const void* x_scale, float* y, int bits,
+                      void* hip_stream) {
+  return gemv_call(h, x, x_scale, true, y, bits, hip_stream);
 }
 
 int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int bits,

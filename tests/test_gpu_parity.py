@@ -245,6 +245,10 @@ def test_error_codes(pwo):
     with pytest.raises(pwo.StagQError) as e:
         m.decode_codes(7)
     assert e.value.status == -2
+    with pytest.raises(pwo.StagQError) as e:
+        m.gemv(xd, 3, x_scale=xbig[1:])          # misaligned scale
+    assert e.value.status == -5
+    assert pwo.lib().stagq_gemv_scaled(m._h, xd.data_ptr(), None, xd.data_ptr(), 3, None) == -1
 
 
 def test_side_wave_reads_x_from_lds_or_global(pwo, monkeypatch):
@@ -288,3 +292,36 @@ def test_stream_read_ceiling_kernel(pwo):
     pwo.stream_read(buf, 16, (1 << 20) + 48, sink)
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
+
+
+@pytest.mark.parametrize("side", ["0", "1"])
+def test_awq_scaled_gemv(pwo, side, monkeypatch):
+    """The run-time inverse AWQ scale folded into x staging (stagq_gemv_scaled)
+    against the oracle's gemv_scaled on ragged, wide and skewed-side-record
+    shapes, in both side-record modes; a unit scale gives the plain GEMV
+    bitwise; the side-record wave's global-x fallback scales x_c the same way."""
+    import torch
+    monkeypatch.setenv("STAGQ_SIDE", side)
+    rng = np.random.default_rng(23)
+    for case in ((1001, 384, 64, 4, 0.01, "student_t", 2), (2048, 1024, 128, 4, 0.02, "student_t", 11),
+                 (64, 4096, 128, 6, 0.1, "normal_outliers", 5)):
+        R, Cc, g, N, frac, dist, seed = case
+        w, x = synth_matrix(R, Cc, dist, seed)
+        F = oracle.encode(w, g, N, frac)
+        a = rng.uniform(0.25, 4.0, Cc).astype(np.float16)
+        m = pwo.StagQMatrix.pack(F)
+        xd, ad = _to_dev(x), _to_dev(a)
+        one = _to_dev(np.ones(Cc, np.float16))
+        xs = oracle.scale_x(x, a)
+        for M in range(2, N + 1):
+            _say(f"awq scaled {case} side={side}", f"bits={M}")
+            y = m.gemv(xd, M, x_scale=ad).cpu().numpy()
+            ref = oracle.gemv_scaled(F, x, a, M)
+            assert _rel(y, ref) <= REL_L2_CONTRACT
+            assert _regression_ok(y, ref, F, xs, M)
+            assert np.array_equal(m.gemv(xd, M, x_scale=one).cpu().numpy(), m.gemv(xd, M).cpu().numpy())
+            if side == "1":
+                monkeypatch.setenv("STAGQ_FLAG_SPINS", "0")
+                assert np.array_equal(m.gemv(xd, M, x_scale=ad).cpu().numpy(), y)
+                monkeypatch.delenv("STAGQ_FLAG_SPINS")
+        torch.cuda.synchronize()
