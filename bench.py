@@ -177,13 +177,25 @@ def sweep(args):
                 entry["bits"][str(M)] = {"us": round(us, 3), "bytes": int(b), "gbps": round(b / us / 1e3, 1),
                                          "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2),
                                          "launch": pwo.plan_gemv(mat.rows, mat.cols, wl.group, wl.nbits, M)}
+            if wname == "mlp":
+                # the same GEMVs with the inverse AWQ scale applied to x (stagq_gemv_scaled)
+                sc = torch.from_numpy(np.full(mat.cols, 0.5, np.float16).view(np.int16)).view(torch.float16).to(dev)
+
+                def launch_sc(c, M):
+                    copies[c].gemv(xd, M, y=ys[c], x_scale=sc)
+
+                for M in wl.bits:
+                    us = graph_time(launch_sc, n_copies, args.steps, [M])
+                    entry["bits"][str(M)]["awq_scaled_us"] = round(us, 3)
             if wname == "layer_sweep":
                 us = graph_time(launch, n_copies, args.steps, list(wl.bits))
                 b = sum(base.bytes_read[M] for M in wl.bits) / len(wl.bits)
                 entry["switched_2_3_4"] = {"us_per_call": round(us, 3), "gbps": round(b / us / 1e3, 1)}
             rows.append(entry)
             print(f"[sweep] {wname}/{mat.name} {mat.rows}x{mat.cols}: " +
-                  " ".join(f"{M}b {v['us']}us {v['pct_peak']}%" for M, v in entry["bits"].items()),
+                  " ".join(f"{M}b {v['us']}us {v['pct_peak']}%" +
+                           (f" (awq {v['awq_scaled_us']}us)" if "awq_scaled_us" in v else "")
+                           for M, v in entry["bits"].items()),
                   file=sys.stderr, flush=True)
             del copies, base, ys
             torch.cuda.empty_cache()
