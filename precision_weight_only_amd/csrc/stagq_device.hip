@@ -114,14 +114,13 @@ __device__ __forceinline__ void nibbles(uint32_t hw, uint32_t lw, uint32_t& zlo,
 }
 
 struct GemvParams {
-  const uint8_t* s0;       // base stream chunk 0; chunk 1 and planes 3..N follow at a stride of chunk_bytes
-  const uint8_t* meta;
+  const uint8_t* units;    // the unit array: per (block, quad) group pairs, base chunks 0-1, planes 3..N
   const uint8_t* row_ptr;
   const uint8_t* side;     // side record, one u64 per entry
   const uint32_t* x;       // fp16 pairs
   const uint32_t* xsc;     // fp16 pairs: inverse AWQ scale per input channel (scaled GEMV only)
   float* y;
-  uint32_t chunk_bytes, meta_bytes, side_bytes, rp_bytes, x_bytes;
+  uint32_t unit_bytes, units_bytes, side_bytes, rp_bytes, x_bytes;
   int32_t R, C, T, T4, S;  // rows, cols, tiles per row (padded to a multiple of 4), waves per workgroup
   int32_t g;
   uint32_t lds_part;          // LDS offset of the lane partials (x and sum(x) at 0)
@@ -137,33 +136,33 @@ struct Slot {
   uint32_t meta[GU];                 // (lo | s << 16) of the tile's groups
 };
 
-// Loads of step i of a wave: the lane's tile is its step-0 tile plus 64 i.
-// rW covers the base stream and the planes, which follow each other at a
-// stride of chunk bytes; stream k and step i are a scalar offset
-// (k chunk + 1024 i) on the lane's fixed voffset vW (vM for the group pairs).
-// A step past the wave's last (ok false, wave-uniform) reads zeros: its
-// voffset is out of range.
+// Loads of one wave step: its unit starts at byte uo (scalar) of rU; the
+// lane's slot is its lane index, at voffset vW = 256 GU + 16 lane in each
+// 1 KB chunk stretch (base chunk 0 at +0, chunk 1 at +1024, plane k at
+// +(k - 1) 1024, scalar offsets) and vM = 4 GU lane among the group pairs.
+// So the step reads one contiguous piece of 256 GU + 1024 M bytes.  A step
+// past the wave's last (ok false, wave-uniform) reads zeros: its voffsets are
+// out of range.
 template <int M, int GU>
-__device__ __forceinline__ void issue(Slot<M, GU>& s, const rsrc_t& rW, uint32_t chunk,
-                                      const rsrc_t& rMeta, uint32_t vW, uint32_t vM, int i, bool ok) {
+__device__ __forceinline__ void issue(Slot<M, GU>& s, const rsrc_t& rU, uint32_t uo, uint32_t vW,
+                                      uint32_t vM, bool ok) {
   const uint32_t off = ok ? vW : kOOB;
-  const int so = i * 1024;
-  s.a = __builtin_amdgcn_raw_buffer_load_b128(rW, off, so, 0);
-  s.b = __builtin_amdgcn_raw_buffer_load_b128(rW, off, int(chunk) + so, 0);
-#pragma unroll
-  for (int k = 0; k < M - 2; k++)
-    s.pl[k] = __builtin_amdgcn_raw_buffer_load_b128(rW, off, int((k + 2) * chunk) + so, 0);
+  const int so = int(uo);
   const uint32_t offm = ok ? vM : kOOB;
-  const int som = i * (256 * GU);
   if constexpr (GU == 1) {
-    s.meta[0] = __builtin_amdgcn_raw_buffer_load_b32(rMeta, offm, som, 0);
+    s.meta[0] = __builtin_amdgcn_raw_buffer_load_b32(rU, offm, so, 0);
   } else if constexpr (GU == 2) {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rMeta, offm, som, 0);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rU, offm, so, 0);
     s.meta[0] = v[0]; s.meta[1] = v[1];
   } else {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rMeta, offm, som, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rU, offm, so, 0);
     s.meta[0] = v[0]; s.meta[1] = v[1]; s.meta[2] = v[2]; s.meta[3] = v[3];
   }
+  s.a = __builtin_amdgcn_raw_buffer_load_b128(rU, off, so, 0);
+  s.b = __builtin_amdgcn_raw_buffer_load_b128(rU, off, so + 1024, 0);
+#pragma unroll
+  for (int k = 0; k < M - 2; k++)
+    s.pl[k] = __builtin_amdgcn_raw_buffer_load_b128(rU, off, so + (k + 2) * 1024, 0);
 }
 
 __device__ __forceinline__ uint32_t s0_dword(const u32x4& a, const u32x4& b, int dw) {
@@ -491,11 +490,10 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   const int cg = lane >> 4;                       // tile column within the four
   const int Q = (p.T + 3) >> 2;                    // groups of four tile columns
   const int q0 = (w * Q) / p.S, nq = ((w + 1) * Q) / p.S - q0;
-  const uint32_t ubase = uint32_t(blk * p.T4 + 4 * q0) * 16u + uint32_t(lane);  // tile of step 0
-  const uint32_t vW = ubase * 16u, vM = ubase * (4u * GU);
-  const uint32_t chunk = p.chunk_bytes;
-  const rsrc_t rW = mk(p.s0, uint32_t(M) * chunk);
-  const rsrc_t rMeta = mk(p.meta, p.meta_bytes);
+  // the wave's first unit, and the lane's voffsets in a unit
+  const uint32_t uo0 = uint32_t(blk * Q + q0) * p.unit_bytes;
+  const uint32_t vW = 256u * GU + 16u * uint32_t(lane), vM = 4u * GU * uint32_t(lane);
+  const rsrc_t rU = mk(p.units, p.units_bytes);
   auto valid = [&](int i) { return i < nq; };   // (tile columns past the row's end are zero tiles)
 
   // --- prologue, in arrival order: (in-workgroup mode) the block's row_ptr,
@@ -524,7 +522,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   }
   __builtin_amdgcn_sched_barrier(0);
   Slot<M, GU> sl[D];
-  issue(sl[0], rW, chunk, rMeta, vW, vM, 0, valid(0));
+  issue(sl[0], rU, uo0, vW, vM, valid(0));
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (SIDE) {                  // this wave's x-staged flag is cleared for the side wave
     flag_s[w] = 0;
@@ -597,7 +595,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   // earlier waves' later steps)
 #pragma unroll
   for (int i = 1; i < D; i++) {
-    issue(sl[i], rW, chunk, rMeta, vW, vM, i, valid(i));
+    issue(sl[i], rU, uo0 + uint32_t(i) * p.unit_bytes, vW, vM, valid(i));
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -611,7 +609,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   auto step = [&](Slot<M, GU>& s, int i) {
     if (i < nq) part = tile_partial<M, GU>(s, xs + xo0 + 4 * kXPitch * i, part);
     __builtin_amdgcn_sched_barrier(0);   // reuse the slot's registers: no loads hoisted above
-    issue(s, rW, chunk, rMeta, vW, vM, i + D, valid(i + D));
+    issue(s, rU, uo0 + uint32_t(i + D) * p.unit_bytes, vW, vM, valid(i + D));
   };
 #pragma unroll
   for (int i = 0; i < D; i++) step(sl[i], i);
@@ -706,27 +704,28 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const uint8_t* buf, ui
 // Code dump: one thread per (padded) tile writes the 128 codes u_M (Eq. 8) of
 // its tile, read field by field from the base stream and planes 3..M.
 struct CodesParams {
-  const uint8_t* s0;
-  const uint8_t* planes;
+  const uint8_t* units;
   uint8_t* codes;
-  uint32_t chunk_bytes;
-  int32_t R, T, T4, C;
-  int64_t tiles;
+  uint32_t unit_bytes, unit_meta, units_bytes;
+  int32_t R, T, Q, C;
+  int64_t tiles;           // units * 64
 };
 
 template <int M>
 __global__ void __launch_bounds__(256) codes_kernel(const CodesParams p) {
-  const int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;   // unit * 64 + slot
   if (u >= p.tiles) return;
-  const int64_t row = (u / (16 * int64_t(p.T4))) * 16 + (u & 15);
-  const int64_t tc = (u >> 4) % p.T4;
+  const int64_t unit = u >> 6;
+  const int t = int(u & 63);
+  const int64_t row = (unit / p.Q) * 16 + (t & 15);
+  const int64_t tc = (unit % p.Q) * 4 + (t >> 4);
   if (row >= p.R || tc >= p.T) return;   // padding rows and zero tiles
-  const rsrc_t rA = mk(p.s0, p.chunk_bytes), rB = mk(p.s0 + p.chunk_bytes, p.chunk_bytes);
-  const uint32_t off = uint32_t(u) * 16u;
-  const u32x4 a = ld128(rA, off), b = ld128(rB, off);
+  const rsrc_t rU = mk(p.units, p.units_bytes);
+  const uint32_t off = uint32_t(unit) * p.unit_bytes + p.unit_meta + uint32_t(t) * 16u;
+  const u32x4 a = ld128(rU, off), b = ld128(rU, off + 1024u);
   u32x4 pl[M > 2 ? M - 2 : 1];
 #pragma unroll
-  for (int k = 0; k < M - 2; k++) pl[k] = ld128(mk(p.planes + uint64_t(k) * p.chunk_bytes, p.chunk_bytes), off);
+  for (int k = 0; k < M - 2; k++) pl[k] = ld128(rU, off + uint32_t(k + 2) * 1024u);
   u32x4* dst = reinterpret_cast<u32x4*>(p.codes + row * p.C + tc * 128);
 #pragma unroll
   for (int i = 0; i < 8; i++) {          // columns 16i .. 16i + 15 (S0 dword i)
@@ -955,15 +954,14 @@ static int gemv_call(stagq_handle h, const void* x, const void* x_scale, bool sc
   LaunchCfg c;
   if (!plan_gemv(H, bits, &c)) return STAGQ_ESHAPE;
   const uint8_t* b = h->dev;
-  c.prm.s0 = b + H.off_s0;
-  c.prm.meta = b + H.off_meta;
+  c.prm.units = b + H.off_units;
   c.prm.row_ptr = b + H.off_rowptr;
   c.prm.side = b + H.off_side;
   c.prm.x = static_cast<const uint32_t*>(x);
   c.prm.xsc = scaled ? static_cast<const uint32_t*>(x_scale) : nullptr;
   c.prm.y = y;
-  c.prm.chunk_bytes = uint32_t(H.bytes_s0_chunk);
-  c.prm.meta_bytes = uint32_t(H.bytes_meta);
+  c.prm.unit_bytes = uint32_t(H.unit_bytes);
+  c.prm.units_bytes = uint32_t(uint64_t(H.blocks) * H.quads * H.unit_bytes);
   c.prm.side_bytes = uint32_t(H.nnz * 8);
   c.prm.rp_bytes = uint32_t((int64_t(H.rows) + 1) * 4);
   c.prm.x_bytes = uint32_t(H.cols * 2);
@@ -1022,13 +1020,14 @@ int stagq_decode_codes(stagq_handle h, int bits, uint8_t* codes, void* hip_strea
   if (!codes) return STAGQ_EINVAL;
   if (reinterpret_cast<uintptr_t>(codes) % 16) return STAGQ_EALIGN;
   dev::CodesParams p;
-  p.s0 = h->dev + H.off_s0;
-  p.planes = h->dev + H.off_planes;
+  p.units = h->dev + H.off_units;
   p.codes = codes;
-  p.chunk_bytes = uint32_t(H.bytes_s0_chunk);
+  p.unit_bytes = uint32_t(H.unit_bytes);
+  p.unit_meta = uint32_t(H.unit_meta_bytes);
+  p.units_bytes = uint32_t(uint64_t(H.blocks) * H.quads * H.unit_bytes);
   p.R = H.rows;
   p.T = H.cols / kTileCols;
-  p.T4 = int32_t(padded_tcols(H.cols));
+  p.Q = H.quads;
   p.C = H.cols;
   p.tiles = H.tiles;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);

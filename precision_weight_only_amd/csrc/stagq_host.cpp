@@ -93,28 +93,27 @@ uint64_t bytes_read(const ImageHeader& h, int bits) {
 // Writes the tiles of rows [r0, r1) (all tile columns).
 static void pack_rows(const stagq_fields* f, const ImageHeader& h, uint8_t* img, int64_t r0,
                       int64_t r1) {
-  const int64_t C = f->cols, n = int64_t(f->rows) * C, T = C / kTileCols, T4 = padded_tcols(C);
+  const int64_t C = f->cols, n = int64_t(f->rows) * C, T = C / kTileCols;
   const int N = f->nbits_max, GU = kTileCols / f->group, G = C / f->group;
-  uint32_t* s0a = reinterpret_cast<uint32_t*>(img + h.off_s0);
-  uint32_t* s0b = reinterpret_cast<uint32_t*>(img + h.off_s0 + h.bytes_s0_chunk);
-  uint32_t* meta = reinterpret_cast<uint32_t*>(img + h.off_meta);
+  auto put = [&](uint64_t off, uint32_t v) { memcpy(img + off, &v, 4); };
   for (int64_t r = r0; r < r1; r++)
     for (int64_t t = 0; t < T; t++) {
-      const int64_t u = tile_index(r, t, T4), c0 = t * kTileCols;
+      const uint64_t uo = unit_offset(h, r, t);
+      const int sl = unit_slot(r, t);
+      const int64_t c0 = t * kTileCols;
       const uint8_t* q = f->q + r * C + c0;
       uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int c = 0; c < kTileCols; c++) w[col_dword(c)] |= uint32_t(q[c]) << (2 * col_field(c));
-      for (int dw = 0; dw < 8; dw++) (dw < 4 ? s0a : s0b)[u * 4 + (dw & 3)] = w[dw];
+      for (int dw = 0; dw < 8; dw++) put(uo + unit_base_dword(h, sl, dw), w[dw]);
       for (int k = 3; k <= N; k++) {
-        uint32_t* pl = reinterpret_cast<uint32_t*>(img + h.off_planes + uint64_t(k - 3) * h.bytes_plane);
         const uint8_t* b = f->planes + int64_t(k - 3) * n + r * C + c0;
         uint32_t pw[4] = {0, 0, 0, 0};
         for (int c = 0; c < kTileCols; c++) pw[c >> 5] |= uint32_t(b[c]) << col_plane_bit(c);
-        for (int d = 0; d < 4; d++) pl[u * 4 + d] = pw[d];
+        for (int d = 0; d < 4; d++) put(uo + unit_plane_dword(h, k, sl, d), pw[d]);
       }
       for (int gi = 0; gi < GU; gi++) {
         const int64_t gidx = r * G + t * GU + gi;
-        meta[u * GU + gi] = uint32_t(f->lo[gidx]) | (uint32_t(f->s[gidx]) << 16);
+        put(uo + unit_pair(h, sl, gi), uint32_t(f->lo[gidx]) | (uint32_t(f->s[gidx]) << 16));
       }
     }
 }
@@ -213,26 +212,24 @@ int stagq_unpack_host(const void* image, size_t image_bytes, stagq_info* shape, 
   shape->nnz = h.nnz; shape->image_bytes = h.total;
   for (int b = 2; b <= h.nbits; b++) shape->bytes_read[b] = bytes_read(h, b);
   const uint8_t* img = static_cast<const uint8_t*>(image);
-  const int64_t R = h.rows, C = h.cols, T = C / kTileCols, T4 = padded_tcols(C), n = R * C;
+  const int64_t R = h.rows, C = h.cols, T = C / kTileCols, n = R * C;
   const int GU = kTileCols / h.group, G = int(C / h.group);
-  const uint32_t* s0a = reinterpret_cast<const uint32_t*>(img + h.off_s0);
-  const uint32_t* s0b = reinterpret_cast<const uint32_t*>(img + h.off_s0 + h.bytes_s0_chunk);
-  const uint32_t* meta = reinterpret_cast<const uint32_t*>(img + h.off_meta);
+  auto get = [&](uint64_t off) { uint32_t v; memcpy(&v, img + off, 4); return v; };
   for (int64_t r = 0; r < R; r++)
     for (int64_t t = 0; t < T; t++) {
-      const int64_t u = tile_index(r, t, T4), c0 = t * kTileCols;
+      const uint64_t uo = unit_offset(h, r, t);
+      const int sl = unit_slot(r, t);
+      const int64_t c0 = t * kTileCols;
       for (int c = 0; c < kTileCols; c++) {
         const int dw = col_dword(c);
-        if (q) q[r * C + c0 + c] = uint8_t(((dw < 4 ? s0a : s0b)[u * 4 + (dw & 3)] >> (2 * col_field(c))) & 3);
+        if (q) q[r * C + c0 + c] = uint8_t((get(uo + unit_base_dword(h, sl, dw)) >> (2 * col_field(c))) & 3);
         if (planes)
-          for (int k = 3; k <= h.nbits; k++) {
-            const uint32_t* pl =
-                reinterpret_cast<const uint32_t*>(img + h.off_planes + uint64_t(k - 3) * h.bytes_plane);
-            planes[int64_t(k - 3) * n + r * C + c0 + c] = uint8_t((pl[u * 4 + (c >> 5)] >> col_plane_bit(c)) & 1);
-          }
+          for (int k = 3; k <= h.nbits; k++)
+            planes[int64_t(k - 3) * n + r * C + c0 + c] =
+                uint8_t((get(uo + unit_plane_dword(h, k, sl, c >> 5)) >> col_plane_bit(c)) & 1);
       }
       for (int gi = 0; gi < GU; gi++) {
-        const uint32_t mw = meta[u * GU + gi];
+        const uint32_t mw = get(uo + unit_pair(h, sl, gi));
         if (lo) lo[r * G + t * GU + gi] = uint16_t(mw & 0xffff);
         if (s) s[r * G + t * GU + gi] = uint16_t(mw >> 16);
       }

@@ -76,26 +76,29 @@ def test_pack_roundtrip_and_size():
 
 
 def test_plane_major_layout_offsets():
-    """A read at precision M touches the base stream and planes 3..M only: the
-    planes follow the base stream in order of k.  Streams hold the rows padded
-    to a multiple of 16 and the 128-column tiles of a row padded to a multiple
-    of 4, 16 bytes per tile."""
+    """A read at precision M touches the first 256 g' + 1024 M bytes of every
+    unit (16 rows x 4 tile columns): the group pairs, then the base stream's
+    two chunk stretches, then planes 3..N in order of k.  Rows are padded to a
+    multiple of 16 and the 128-column tiles of a row to a multiple of 4."""
     w, _ = synth_matrix(13, 256, "student_t", 4)
     F = oracle.encode(w, 128, 6, 0.0)
     img = pwo.pack_host(F)
     hdr = np.frombuffer(img[:256].tobytes(), dtype=np.uint64)
-    off_s0, off_planes = int(hdr[6]), int(hdr[7])
-    chunk, plane = int(hdr[13]), int(hdr[14])
-    assert chunk == plane == 16 * 4 * 16        # 13 rows padded to 16, 2 tiles per row padded to 4
-    assert off_planes - off_s0 == 2 * chunk
-    # Flipping one refinement bit in the fields changes exactly one byte, in plane 5.
+    quads = int(hdr[6]) & 0xffffffff
+    off_units, unit_bytes, unit_meta = int(hdr[7]), int(hdr[8]), int(hdr[9])
+    assert quads == 1                           # 2 tiles per row padded to 4
+    assert unit_meta == 64 * 4                  # one fp16 pair per tile (g = 128)
+    assert unit_bytes == unit_meta + 6 * 1024   # base (2 x 1 KB) + planes 3..6
+    # Flipping one refinement bit (plane 5, row 3, column 77) changes exactly
+    # one byte: in plane 5's stretch of the unit, at slot 3, dword 77 // 32.
     F2 = oracle.Fields(**{**F.__dict__})
     F2.planes = F.planes.copy()
     F2.planes[2, 3, 77] ^= 1
     img2 = pwo.pack_host(F2)
     diff = np.nonzero(img != img2)[0]
     assert diff.size == 1
-    assert off_planes + 2 * plane <= diff[0] < off_planes + 3 * plane
+    o = off_units + unit_meta + 4 * 1024 + 3 * 16 + 2 * 4
+    assert o <= diff[0] < o + 4
 
 
 def test_bytes_read_model():
