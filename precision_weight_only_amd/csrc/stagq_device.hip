@@ -782,12 +782,16 @@ static int env_int(const char* name, int dflt) {
   return e ? atoi(e) : dflt;
 }
 
-// Steps of loads in flight per wave, per precision.  Shallow on purpose: with
+// Steps of loads in flight per wave, per precision, for the side-record-wave
+// grids (many blocks) and the in-workgroup ones.  Shallow on purpose: with
 // two to four waves per SIMD the chip holds enough bytes in flight, and
-// deeper per-wave queues only delay every wave's first data (measured on the
-// 14336 x 4096 and 4096 x 14336 shapes: depth 2 beats 3 and 4 at two bits,
-// depth 1 beats 2 at four bits).
-constexpr int kDepth[9] = {0, 0, 2, 2, 1, 1, 1, 1, 1};
+// deeper per-wave queues only delay every wave's first data.  Measured: depth
+// 2 beats 3 and 4 at 2-3 bits (14336 x 4096, 4096 x 14336); at 4 bits depth 2
+// beats 1 on the many-block grids (17920 x 5120: 12.5 against 13.4 us; equal
+// on 14336 x 4096) but loses on 5120 x 17920 (17.3 against 15.7 us); from 5
+// bits depth 1 wins.
+constexpr int kDepthSide[9] = {0, 0, 2, 2, 2, 1, 1, 1, 1};
+constexpr int kDepthInWg[9] = {0, 0, 2, 2, 1, 1, 1, 1, 1};
 constexpr int kMaxWaves = 16;   // waves per workgroup (incl. a side-record wave): __launch_bounds__(1024)
 
 // LDS carve-up: per tile (padded tile columns, plus a spare tile) 64 dwords
@@ -813,10 +817,10 @@ static size_t lds_layout(int C, int S, dev::GemvParams* prm) {
 // waves on every SIMD (8 per CU), within [ceil(groups / 4), min(16, groups)]
 // (a wave stages the x of at most 4 steps).  With at least two workgroups per
 // CU the side record goes to an extra wave (its latency then hides behind
-// other workgroups; with fewer it would sit on the critical path), and below
-// 4 bits, where a step is cheapest, each wave takes the most steps it can
-// (measured on 14336 x 4096: 7.2 / 8.2 us at 2 / 3 bits against 7.6 / 8.6
-// with two waves per SIMD; at 4 bits two waves per SIMD stay ahead).
+// other workgroups; with fewer it would sit on the critical path), and up to
+// 4 bits each wave then takes the most steps it can (measured on 14336 x 4096:
+// 7.2 / 8.2 us at 2 / 3 bits against 7.6 / 8.6 with two waves per SIMD; at 4
+// bits, with two steps in flight, equal).
 // STAGQ_WAVES and STAGQ_SIDE override the choices (tuning); STAGQ_FLAG_SPINS
 // sets the side-record wave's spin limit (testing its global-x fallback).
 static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
@@ -833,7 +837,7 @@ static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   if (smin > smax) return false;
   const int target = 2 * 4 * cus;
   int S = (target + nblk - 1) / nblk;
-  if (side && bits <= 3) S = smin;
+  if (side && bits <= 4) S = smin;
   S = std::max(smin, std::min(smax, S));
   c->prm.flag_spins = env_int("STAGQ_FLAG_SPINS", dev::kFlagSpins);
   const int s_env = env_int("STAGQ_WAVES", 0);
@@ -866,7 +870,7 @@ static hipError_t launch_gemv(const LaunchCfg& c, hipStream_t st) {
 
 template <int M, int GU>
 static hipError_t launch_gemv_d(const LaunchCfg& c, hipStream_t st) {
-  return launch_gemv<M, GU, kDepth[M]>(c, st);
+  return c.side ? launch_gemv<M, GU, kDepthSide[M]>(c, st) : launch_gemv<M, GU, kDepthInWg[M]>(c, st);
 }
 
 template <int M>
@@ -997,7 +1001,7 @@ int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, in
   LaunchCfg c;
   if (!plan_gemv(H, bits, &c)) return STAGQ_ESHAPE;
   out[0] = c.grid; out[1] = 64 * (c.S + (c.side ? 1 : 0)); out[2] = c.S; out[3] = c.nt_max;
-  out[4] = kBlockRows; out[5] = int32_t(c.lds); out[6] = c.side ? 1 : 0; out[7] = kDepth[bits];
+  out[4] = kBlockRows; out[5] = int32_t(c.lds); out[6] = c.side ? 1 : 0; out[7] = c.side ? kDepthSide[bits] : kDepthInWg[bits];
   return STAGQ_OK;
 }
 

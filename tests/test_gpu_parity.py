@@ -117,7 +117,10 @@ def test_layer_sweep_bits_switched_per_call(pwo, mname):
         assert _regression_ok(y.cpu().numpy(), refs[M], F, x, M)
     for M in wl.bits:  # same bits -> bitwise identical results
         same = [y.cpu().numpy() for b, y in ys if b == M]
-        assert all(np.array_equal(same[0], s) for s in same[1:])
+        for i, s in enumerate(same[1:], 1):
+            d = np.nonzero(same[0] != s)[0]
+            assert d.size == 0, (f"bits={M}: call {i} differs from call 0 in {d.size} rows, e.g. "
+                                 f"{d[:8].tolist()}: {same[0][d[:4]].tolist()} vs {s[d[:4]].tolist()}")
 
 
 def _tile_rows(F, reps, rows):

@@ -159,15 +159,16 @@ def test_strerror_covers_every_status():
 def test_launch_plan_shapes():
     """Launch shapes for a 256-CU device (the host-only default): one
     workgroup per 16-row block; with two or more blocks per CU the side record
-    runs on an extra wave and, below 4 bits, each wave takes the most steps
-    it can (4, as x is staged for at most 4 steps)."""
+    runs on an extra wave and, up to 4 bits, each wave takes the most steps it
+    can (4, as x is staged for at most 4 steps)."""
     def plan(R, Cc, bits, g=128, N=4):
         out = (C.c_int32 * 8)()
         assert pwo.lib().stagq_plan_gemv(R, Cc, g, N, bits, out) == 0
         return dict(grid=out[0], threads=out[1], S=out[2], steps=out[3], side=out[6])
-    p2, p4 = plan(14336, 4096, 2), plan(14336, 4096, 4)
+    p2, p4, p5 = plan(14336, 4096, 2), plan(14336, 4096, 4), plan(14336, 4096, 5, N=6)
     assert (p2["grid"], p2["S"], p2["steps"], p2["side"], p2["threads"]) == (896, 2, 4, 1, 192)
-    assert (p4["S"], p4["steps"], p4["threads"]) == (3, 3, 256)
+    assert (p4["S"], p4["steps"], p4["threads"]) == (2, 4, 192)
+    assert (p5["S"], p5["steps"], p5["threads"]) == (3, 3, 256)
     d = plan(4096, 14336, 2)
     assert (d["grid"], d["S"], d["side"], d["threads"]) == (256, 8, 0, 512)
     lm = plan(128256, 4096, 3)
