@@ -5,5 +5,5 @@ package.  It shares no code with the HIP library.
 """
 from .stagq_oracle import (  # noqa: F401
     Fields, encode, quantize_value, codes, w_main, w_hat, gemv, half_step, affine_pair, budget,
-    scale_x, gemv_scaled,
+    scale_x, gemv_scaled, initial_pair, uniform_codebooks, codebook_table, pair_loss,
 )

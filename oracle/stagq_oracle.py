@@ -55,6 +55,15 @@ R7  A group whose stored step is 0 gets q = 0 and all-zero planes.
 R8  The run-time inverse scale arrives as one fp16 factor per input channel
     (1 / a_c), and the scaled activation is the fp16 rounding (nearest, ties to
     even) of the exact product x_c * (1 / a_c): the GEMV's activations are fp16.
+R9  Codebook metadata: the initial pair (Appendix B) puts the outer two of four
+    symmetric levels 6% of the group range in from either end, so its step is
+    0.88 / 3 = 0.2933 of the range (the page's "0.29").
+R10 The 256 (lo, s) pairs are s = fp16(2^c_s[i]) and lo = fp16(c_r[j] * s) from
+    the fp16 codebook entries, and index i * 16 + j is the stored byte.  Of the
+    page's three placement rules only uniform placement (its fallback) is used.
+R11 In the per-group loss, the pre-grid entry "clipped to the next value
+    inward" is clamped to the range of the group's other entries; E_c = 1 (no
+    calibration data); lambda = 4; the lowest index wins ties.
 
 Parity status of every function is recorded next to it ("pinned by ...").
 """
@@ -68,6 +77,7 @@ import numpy as np
 __all__ = [
     "Fields", "encode", "quantize_value", "codes", "w_main", "w_hat", "gemv",
     "half_step", "affine_pair", "budget", "scale_x", "gemv_scaled",
+    "initial_pair", "uniform_codebooks", "codebook_table", "pair_loss",
 ]
 
 
@@ -88,6 +98,11 @@ class Fields:
     val: np.ndarray            # float16 [nnz], the recorded value P
     n_pre: int = 0             # entries held out by the pre-grid guard
     n_post: int = 0            # entries held out by the post-grid guard
+    # codebook metadata (encode(..., pair_fit="codebook") only): per group an
+    # 8-bit index i * 16 + j into two 16-entry fp16 codebooks, log2 s and lo/s
+    idx: Optional[np.ndarray] = None       # uint8 [R, G]
+    cb_log2s: Optional[np.ndarray] = None  # float16 [16]
+    cb_ratio: Optional[np.ndarray] = None  # float16 [16]
 
     @property
     def nnz(self) -> int:
@@ -141,7 +156,82 @@ def affine_pair(lo, s, M: int):
 # Encoder (section 3.6 order).  Pinned by hand-worked small matrices in
 # tests/golden/encoder_small.json, the Figure 1 example and the invariants.
 # ---------------------------------------------------------------------------
-def encode(w16: np.ndarray, group: int, nbits: int, frac: float, T: float = 4.0) -> Fields:
+# ---------------------------------------------------------------------------
+# Codebook metadata (section 3.1, Eq. 5-6, Appendices B and E; readings
+# R9-R11).  Pinned by hand-worked tables, the uniform-placement endpoints,
+# the symmetric initial pair and an exact-rational brute force of the
+# per-group choice.
+# ---------------------------------------------------------------------------
+def initial_pair(vmin, vmax):
+    """The initial pair of Appendix B (never stored): four levels placed
+    symmetrically in [min, max], the outer two 6% of the range in from either
+    end, so s0 = 0.88 (max - min) / 3 and lo0 = min + 0.06 (max - min)
+    (reading R9: the page's "step 0.29 of the range" is this step rounded)."""
+    rng = np.asarray(vmax, dtype=np.float64) - np.asarray(vmin, dtype=np.float64)
+    return np.asarray(vmin, dtype=np.float64) + 0.06 * rng, 0.88 * rng / 3.0
+
+
+def uniform_codebooks(lo0, s0):
+    """Two 16-entry codebooks placed uniformly over the range of the initial
+    pairs (Appendix E's uniform rule): log2 s over [min, max] of log2 s0, and
+    lo/s over [min, max] of lo0 / s0, groups with s0 > 0 only; stored as fp16."""
+    lo0 = np.asarray(lo0, dtype=np.float64).ravel()
+    s0 = np.asarray(s0, dtype=np.float64).ravel()
+    pos = s0 > 0.0
+    if not pos.any():
+        return np.zeros(16, np.float16), np.zeros(16, np.float16)
+    L = np.log2(s0[pos])
+    P = lo0[pos] / s0[pos]
+    t = np.arange(16, dtype=np.float64) / 15.0
+    return ((L.min() + t * (L.max() - L.min())).astype(np.float16),
+            (P.min() + t * (P.max() - P.min())).astype(np.float16))
+
+
+def codebook_table(cb_log2s, cb_ratio):
+    """The 256 (lo, s) pairs the codebooks span (reading R10): for index
+    i * 16 + j, s = fp16(2^cb_log2s[i]) and lo = fp16(cb_ratio[j] * s), each
+    computed in float64 from the fp16 inputs and rounded once."""
+    L = np.asarray(cb_log2s, dtype=np.float16).astype(np.float64)
+    P = np.asarray(cb_ratio, dtype=np.float16).astype(np.float64)
+    s = np.exp2(L).astype(np.float16)
+    lo = (P[None, :] * s.astype(np.float64)[:, None]).astype(np.float16)
+    return lo.reshape(256), np.repeat(s, 16)
+
+
+def pair_loss(v, lo, s, nbits: int, lam: float = 4.0):
+    """D(lo, s) of Eq. (5) with E_c = 1 over the last axis of v: the mean over
+    M = 2..N of the squared reconstruction errors plus lam times the floor
+    term of Eq. (6), rho = s sum_{k=3..N} 2^-(k-1).  lo, s broadcast against
+    v's leading axes."""
+    v = np.asarray(v, dtype=np.float64)
+    lo = np.asarray(lo, dtype=np.float64)[..., None]
+    s = np.asarray(s, dtype=np.float64)[..., None]
+    d = v - lo
+    q = np.zeros(v.shape, dtype=np.float64)
+    for j in range(3):
+        q += (d >= (j + 0.5) * s)
+    q = np.where(s > 0.0, q, 0.0)
+    rec = lo + s * q
+    rho = s * sum(2.0 ** -(k - 1) for k in range(3, nbits + 1))
+    floor = (np.maximum(np.abs(v - rec) - rho, 0.0) ** 2).sum(axis=-1)
+    err = ((v - rec) ** 2).sum(axis=-1)
+    for k in range(3, nbits + 1):
+        b = (v - rec) >= 0.0
+        rec = rec + np.where(s > 0.0, (2.0 * b - 1.0) * s / 2.0 ** (k - 1), 0.0)
+        err = err + ((v - rec) ** 2).sum(axis=-1)
+    return err / (nbits - 1) + lam * floor
+
+
+def encode(w16: np.ndarray, group: int, nbits: int, frac: float, T: float = 4.0,
+           pair_fit: str = "minmax", lam: float = 4.0) -> Fields:
+    """The reference encoder.  pair_fit "minmax": the pair of R2, stored as two
+    fp16 numbers per group.  pair_fit "codebook": the pages' metadata (section
+    3.1): codebooks fitted to the initial pairs of Appendix B by uniform
+    placement, then per group the index whose (lo, s) minimizes Eq. (5) (E_c = 1,
+    lambda = lam) over the group with its pre-grid entry clipped to the next
+    value inward (R11); every later step uses the chosen pair."""
+    if pair_fit not in ("minmax", "codebook"):
+        raise ValueError("pair_fit must be 'minmax' or 'codebook'")
     w16 = np.asarray(w16)
     if w16.ndim != 2 or w16.dtype not in (np.float16, np.float64):
         raise ValueError("encode expects a 2-D float16 (or float64, statistics only) matrix")
@@ -178,8 +268,25 @@ def encode(w16: np.ndarray, group: int, nbits: int, frac: float, T: float = 4.0)
     # 2. Pair fit over the entries that stay in the main stream (R2).
     lo64 = np.where(mask, np.inf, wg).min(axis=2)
     hi64 = np.where(mask, -np.inf, wg).max(axis=2)
-    lo16 = lo64.astype(np.float16)                  # exact for fp16 weights
-    s16 = ((hi64 - lo64) / 3.0).astype(np.float16)  # round to nearest even
+    idx = cb_log2s = cb_ratio = None
+    if pair_fit == "minmax":
+        lo16 = lo64.astype(np.float16)                  # exact for fp16 weights
+        s16 = ((hi64 - lo64) / 3.0).astype(np.float16)  # round to nearest even
+    else:
+        # the group with its pre-grid entry clipped to the next value inward
+        # (equal to the min / max of the remaining entries), R11
+        v = np.clip(wg, lo64[..., None], hi64[..., None])
+        lo0, s0 = initial_pair(lo64, hi64)
+        cb_log2s, cb_ratio = uniform_codebooks(lo0, s0)
+        tlo, ts = codebook_table(cb_log2s, cb_ratio)
+        best = np.full((R, G), np.inf)
+        idx = np.zeros((R, G), dtype=np.uint8)
+        for c in range(256):                             # lowest index wins ties
+            D = pair_loss(v, np.full((R, G), float(tlo[c])), np.full((R, G), float(ts[c])), nbits, lam)
+            better = D < best
+            best = np.where(better, D, best)
+            idx = np.where(better, np.uint8(c), idx)
+        lo16, s16 = tlo[idx], ts[idx]
     lo_f = lo16.astype(np.float64)[..., None]
     s_f = s16.astype(np.float64)[..., None]
 
@@ -231,6 +338,7 @@ def encode(w16: np.ndarray, group: int, nbits: int, frac: float, T: float = 4.0)
         lo=lo16, s=s16, mask=mask2,
         row_ptr=row_ptr, col=cc.astype(np.int32), val=w16[rr, cc].astype(np.float16),
         n_pre=int(n_pre), n_post=int(max(n_post, 0)),
+        idx=idx, cb_log2s=cb_log2s, cb_ratio=cb_ratio,
     )
 
 

@@ -350,3 +350,89 @@ def test_gemv_scaled_special_cases(tiny_fields):
         dx = float(np.float16(3.0 * float(x[c]))) - float(x[c])
         col = oracle.w_hat(F, M)[:, c]
         assert np.allclose(oracle.gemv_scaled(F, x, a, M) - y, col * dx, rtol=1e-12, atol=1e-12)
+
+
+def test_initial_pair_is_symmetric_with_outer_levels_6pct_in():
+    """Appendix B / reading R9 on a hand-worked group range [-1, 3]: outer levels
+    at -0.76 and 2.76 (6% of the range 4 in from either end), centre level
+    midpoint 1.0 = (min + max) / 2, step 0.88 * 4 / 3."""
+    lo0, s0 = oracle.initial_pair(-1.0, 3.0)
+    assert np.isclose(lo0, -0.76, rtol=0, atol=1e-15)
+    assert np.isclose(s0, 3.52 / 3.0, rtol=0, atol=1e-15)
+    assert np.isclose(lo0 + 3 * s0, 2.76, rtol=0, atol=1e-14)
+    assert np.isclose(lo0 + 1.5 * s0, 1.0, rtol=0, atol=1e-14)
+
+
+def test_uniform_codebooks_span_the_initial_pairs():
+    """Uniform placement: 16 entries from the smallest to the largest log2 s0
+    and lo0/s0, equally spaced (s0 = 0 groups ignored).  With log2 s0 in
+    {-6, -3} the entries are -6 + i/5 (fp16); with lo0/s0 in {-2, 1} they are
+    -2 + i/5."""
+    s0 = np.array([2.0 ** -6, 2.0 ** -3, 0.0])
+    lo0 = np.array([-2.0 * 2.0 ** -6, 1.0 * 2.0 ** -3, 5.0])
+    cs, cr = oracle.uniform_codebooks(lo0, s0)
+    assert cs.dtype == np.float16 and cr.dtype == np.float16
+    assert [float(v) for v in cs] == [float(np.float16(-6 + i / 5)) for i in range(16)]
+    assert [float(v) for v in cr] == [float(np.float16(-2 + i / 5)) for i in range(16)]
+    assert float(cs[0]) == -6.0 and float(cs[15]) == -3.0 and float(cs[5]) == -5.0
+
+
+def test_codebook_table_hand_worked():
+    """Reading R10 on hand-worked entries: index i * 16 + j holds
+    s = fp16(2^c_s[i]), lo = fp16(c_r[j] * s).  2^-6 = 0.015625 exactly and
+    -1.5 * 2^-6 = -0.0234375; 2^-4.5 = 0.0441941738... rounds to
+    1448 / 2^15 = 0.044189453125, and -1.5 times that is -1086 / 2^14, exact."""
+    cs = np.zeros(16, np.float16); cr = np.zeros(16, np.float16)
+    cs[0], cs[1] = -6.0, -4.5
+    cr[0], cr[1] = -1.5, 0.25
+    lo, s = oracle.codebook_table(cs, cr)
+    assert (float(s[0]), float(lo[0])) == (0.015625, -0.0234375)
+    assert (float(s[1]), float(lo[1])) == (0.015625, 0.00390625)
+    assert (float(s[16]), float(lo[16])) == (0.044189453125, -1086 / 2 ** 14)
+    assert (float(s[17]), float(lo[17])) == (0.044189453125, float(np.float16(0.25 * 0.044189453125)))
+
+
+def _exact_pair_loss(vals, lo, s, N, lam=4):
+    """Eq. (5) with E_c = 1 in exact rationals, written independently: nearest
+    base level (ties up), each plane the sign of the prefix residual (0 -> +),
+    squared errors averaged over M = 2..N, plus lam times the floor term."""
+    lo, s = Fraction(lo), Fraction(s)
+    rho = s * sum(Fraction(1, 2 ** (k - 1)) for k in range(3, N + 1))
+    tot, floor = Fraction(0), Fraction(0)
+    for v in vals:
+        v = Fraction(v)
+        q = 0 if s == 0 else min(3, max(0, sum(1 for j in range(3) if v - lo >= (j + Fraction(1, 2)) * s)))
+        rec = lo + s * q
+        floor += max(abs(v - rec) - rho, Fraction(0)) ** 2
+        tot += (v - rec) ** 2
+        for k in range(3, N + 1):
+            step = s / 2 ** (k - 1)
+            rec = rec + step if v - rec >= 0 else rec - step
+            tot += (v - rec) ** 2
+    return tot / (N - 1) + lam * floor
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.02])
+def test_codebook_choice_matches_exact_brute_force(frac):
+    """The per-group index minimizes Eq. (5) over all 256 pairs, checked in
+    exact rationals (lowest index among equal minima); the pre-grid entry, if
+    any, enters the loss clamped to the range of the group's other entries."""
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((3, 16)) * 0.05).astype(np.float16)
+    w[1, 3] = np.float16(0.9)                      # a pre-grid candidate (ratio > 4)
+    N, g = 3, 8
+    F = oracle.encode(w, g, N, frac, pair_fit="codebook")
+    tlo, ts = oracle.codebook_table(F.cb_log2s, F.cb_ratio)
+    assert np.array_equal(F.lo.view(np.uint16), tlo[F.idx].view(np.uint16))
+    assert np.array_equal(F.s.view(np.uint16), ts[F.idx].view(np.uint16))
+    assert F.n_post == 0 and F.n_pre == (1 if frac else 0)   # K = 1: the one pre-grid entry
+    pre = F.mask
+    for r in range(3):
+        for gi in range(2):
+            vals = [float(v) for v in w[r, gi * g:(gi + 1) * g]]
+            keep = [v for v, m in zip(vals, pre[r, gi * g:(gi + 1) * g]) if not m]
+            vals = [min(max(v, min(keep)), max(keep)) for v in vals]
+            losses = [_exact_pair_loss(vals, float(tlo[c]), float(ts[c]), N) for c in range(256)]
+            best = min(losses)
+            assert losses[int(F.idx[r, gi])] == best
+            assert int(F.idx[r, gi]) == losses.index(best)
