@@ -56,6 +56,21 @@ extern "C" {
 typedef struct stagq_handle_s* stagq_handle;
 
 /*
+ * Codebook metadata ([StagQ] section 3.1, Appendix G): two 16-entry fp16
+ * codebooks per matrix, one of log2 s and one of lo / s, and per group an
+ * 8-bit index i * 16 + j.  The pair of index i * 16 + j is
+ * s = fp16(2^log2s[i]), lo = fp16(ratio[j] * s), each rounded once to nearest.
+ *   idx    [rows*(cols/group)]   uint8 index per group
+ *   log2s  [16], ratio [16]       fp16 bits
+ * Host memory, caller-owned, read during the call only.
+ */
+typedef struct {
+  const uint8_t* idx;
+  const uint16_t* log2s;
+  const uint16_t* ratio;
+} stagq_codebook;
+
+/*
  * Unpacked encoder output in host memory, caller-owned, read during the call
  * only.  Layouts are row-major.
  *   q        [rows*cols]                 base codes 0..3
@@ -63,6 +78,9 @@ typedef struct stagq_handle_s* stagq_handle;
  *   lo, s    [rows*(cols/group)]         fp16 bits of the group pair
  *   row_ptr  [rows+1], col [nnz], val [nnz]: the side record P as CSR sorted by
  *            (row, col); val holds the fp16 bits of the recorded weight.
+ *   codebook NULL: the image stores lo, s (4 bytes per group).  Otherwise the
+ *            image stores the codebook metadata (1 byte per group, plus the 256
+ *            pairs once), and lo, s must be the pairs the indices select.
  * The planes must be 0 at held-out positions (section 3.6: the planes skip every
  * position the side record carries); q there is the base code of the original
  * weight.
@@ -77,6 +95,7 @@ typedef struct {
   const int32_t* col;
   const uint16_t* val;
   int64_t nnz;
+  const stagq_codebook* codebook;
 } stagq_fields;
 
 /* Shape and traffic of a packed matrix. */
@@ -85,10 +104,12 @@ typedef struct {
   int64_t nnz;
   uint64_t image_bytes;      /* size of the packed image */
   /* Algorithmic bytes one GEMV at precision b moves, for b = 2..N (index b;
-   * 0 elsewhere): base stream + planes 3..b + group pairs + side record (one
-   * 8-byte entry per held-out weight: column, base code, fp16 value, row) + x
-   * (fp16) + y (fp32). */
+   * 0 elsewhere): base stream + planes 3..b + group metadata (4 bytes per group,
+   * or 1 byte per group plus the 1 KB table of 256 pairs) + row_ptr + side
+   * record (one 8-byte entry per held-out weight) + x (fp16) + y (fp32). */
   uint64_t bytes_read[9];
+  int32_t codebook;          /* 1 if the image stores codebook metadata */
+  int32_t reserved;
 } stagq_info;
 
 /* Bytes of the packed image for these fields (0 if the shape is unsupported). */
@@ -97,9 +118,10 @@ size_t stagq_packed_bytes(const stagq_fields* f);
 /*
  * Validate f and write its packed image into host memory dst (dst_bytes >=
  * stagq_packed_bytes(f), 16-byte aligned).  Pure host code: no HIP call.  The
- * image is plane-major: the base stream, then plane 3, 4, ..., N, then the group
- * pairs and the side record, so a read at precision M touches only the base and
- * planes 3..M (section 3.3: fields stored in plane order).
+ * image is plane-major per unit of 16 rows x 4 tiles of 128 columns: the group
+ * metadata, the base stream, then plane 3, 4, ..., N, so a read at precision M
+ * touches only the metadata, the base and planes 3..M of every unit (section
+ * 3.3: fields stored in plane order); the side record follows the units.
  */
 int stagq_pack_host(const stagq_fields* f, void* dst, size_t dst_bytes);
 

@@ -115,7 +115,7 @@ def unpack_host(image: np.ndarray) -> Dict:
     out["lo"] = out["lo"].view(np.float16)
     out["s"] = out["s"].view(np.float16)
     out["val"] = out["val"].view(np.float16)
-    out.update(rows=R, cols=Cc, group=g, nbits=N, nnz=nnz)
+    out.update(rows=R, cols=Cc, group=g, nbits=N, nnz=nnz, codebook=int(info.codebook))
     return out
 
 
@@ -130,6 +130,7 @@ class StagQMatrix:
         self.nnz = info.nnz
         self.image_bytes = info.image_bytes
         self.bytes_read = {b: int(info.bytes_read[b]) for b in range(2, self.nbits + 1)}
+        self.codebook = bool(info.codebook)    # codebook metadata (else fp16 pairs)
 
     @classmethod
     def pack(cls, fields, device="cuda:0", stream=None) -> "StagQMatrix":

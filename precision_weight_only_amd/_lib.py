@@ -26,11 +26,16 @@ class StagQError(RuntimeError):
         super().__init__(f"{what}: {STATUS.get(status, status)} ({lib().stagq_strerror(status).decode()})")
 
 
+class Codebook(C.Structure):
+    _fields_ = [("idx", C.c_void_p), ("log2s", C.c_void_p), ("ratio", C.c_void_p)]
+
+
 class Fields(C.Structure):
     _fields_ = [
         ("rows", C.c_int32), ("cols", C.c_int32), ("group", C.c_int32), ("nbits_max", C.c_int32),
         ("q", C.c_void_p), ("planes", C.c_void_p), ("lo", C.c_void_p), ("s", C.c_void_p),
         ("row_ptr", C.c_void_p), ("col", C.c_void_p), ("val", C.c_void_p), ("nnz", C.c_int64),
+        ("codebook", C.c_void_p),
     ]
 
 
@@ -38,6 +43,7 @@ class Info(C.Structure):
     _fields_ = [
         ("rows", C.c_int32), ("cols", C.c_int32), ("group", C.c_int32), ("nbits_max", C.c_int32),
         ("nnz", C.c_int64), ("image_bytes", C.c_uint64), ("bytes_read", C.c_uint64 * 9),
+        ("codebook", C.c_int32), ("reserved", C.c_int32),
     ]
 
 
@@ -115,5 +121,14 @@ def fields_struct(f, keep: list) -> Fields:
     nbits = int(get("nbits")) if not isinstance(f, dict) or "nbits" in f else planes.shape[0] + 2
     group = int(get("group"))
     keep.extend([q, planes, lo, s, row_ptr, col, val])
+    cb = None
+    opt = (lambda k: f.get(k)) if isinstance(f, dict) else (lambda k: getattr(f, k, None))
+    if opt("idx") is not None:           # codebook metadata (idx, cb_log2s, cb_ratio)
+        idx = np.ascontiguousarray(opt("idx"), dtype=np.uint8)
+        l2s = np.ascontiguousarray(np.asarray(opt("cb_log2s"), dtype=np.float16).view(np.uint16))
+        rat = np.ascontiguousarray(np.asarray(opt("cb_ratio"), dtype=np.float16).view(np.uint16))
+        cb = Codebook(_ptr(idx), _ptr(l2s), _ptr(rat))
+        keep.extend([idx, l2s, rat, cb])
     return Fields(R, Cc, group, nbits, _ptr(q), _ptr(planes), _ptr(lo), _ptr(s),
-                  row_ptr.ctypes.data_as(C.c_void_p), _ptr(col), _ptr(val), int(col.shape[0]))
+                  row_ptr.ctypes.data_as(C.c_void_p), _ptr(col), _ptr(val), int(col.shape[0]),
+                  C.cast(C.pointer(cb), C.c_void_p) if cb is not None else None)

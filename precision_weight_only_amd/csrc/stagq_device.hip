@@ -114,18 +114,21 @@ __device__ __forceinline__ void nibbles(uint32_t hw, uint32_t lw, uint32_t& zlo,
 }
 
 struct GemvParams {
-  const uint8_t* units;    // the unit array: per (block, quad) group pairs, base chunks 0-1, planes 3..N
+  const uint8_t* units;    // the unit array: per (block, quad) group metadata, base chunks 0-1, planes 3..N
+  const uint32_t* table;   // codebook metadata: the 256 (lo | s << 16) pairs
   const uint8_t* row_ptr;
   const uint8_t* side;     // side record, one u64 per entry
   const uint32_t* x;       // fp16 pairs
   const uint32_t* xsc;     // fp16 pairs: inverse AWQ scale per input channel (scaled GEMV only)
   float* y;
   uint32_t unit_bytes, units_bytes, side_bytes, rp_bytes, x_bytes;
+  uint32_t unit_meta;      // bytes of group metadata at the start of a unit
   int32_t R, C, T, T4, S;  // rows, cols, tiles per row (padded to a multiple of 4), waves per workgroup
   int32_t g;
   uint32_t lds_part;          // LDS offset of the lane partials (x and sum(x) at 0)
   uint32_t lds_rp, lds_runs;  // LDS offsets of the block's row_ptr and the side-record run sums
   uint32_t lds_flag;          // LDS offset of the per-wave x-staged flags (side-record wave mode)
+  uint32_t lds_table;         // LDS offset of the per-wave copies of the 256 pairs (codebook metadata)
   int32_t flag_spins;         // spin limit of the side-record wave's wait for them
 };
 
@@ -137,19 +140,27 @@ struct Slot {
 };
 
 // Loads of one wave step: its unit starts at byte uo (scalar) of rU; the
-// lane's slot is its lane index, at voffset vW = 256 GU + 16 lane in each
-// 1 KB chunk stretch (base chunk 0 at +0, chunk 1 at +1024, plane k at
-// +(k - 1) 1024, scalar offsets) and vM = 4 GU lane among the group pairs.
-// So the step reads one contiguous piece of 256 GU + 1024 M bytes.  A step
-// past the wave's last (ok false, wave-uniform) reads zeros: its voffsets are
-// out of range.
-template <int M, int GU>
+// lane's slot is its lane index, at voffset vW = m + 16 lane in each 1 KB
+// chunk stretch (base chunk 0 at +0, chunk 1 at +1024, plane k at
+// +(k - 1) 1024, scalar offsets; m the unit's metadata bytes) and vM among
+// the group metadata (4 GU lane for pairs, GU lane for codebook indices, CB).
+// So the step reads one contiguous piece of m + 1024 M bytes.  A step past
+// the wave's last (ok false, wave-uniform) reads zeros: its voffsets are out
+// of range.
+template <int M, int GU, bool CB>
 __device__ __forceinline__ void issue(Slot<M, GU>& s, const rsrc_t& rU, uint32_t uo, uint32_t vW,
                                       uint32_t vM, bool ok) {
   const uint32_t off = ok ? vW : kOOB;
   const int so = int(uo);
   const uint32_t offm = ok ? vM : kOOB;
-  if constexpr (GU == 1) {
+  if constexpr (CB) {                    // GU index bytes, kept packed in meta[0]
+    if constexpr (GU == 1)
+      s.meta[0] = __builtin_amdgcn_raw_buffer_load_b8(rU, offm, so, 0);
+    else if constexpr (GU == 2)
+      s.meta[0] = __builtin_amdgcn_raw_buffer_load_b16(rU, offm, so, 0);
+    else
+      s.meta[0] = __builtin_amdgcn_raw_buffer_load_b32(rU, offm, so, 0);
+  } else if constexpr (GU == 1) {
     s.meta[0] = __builtin_amdgcn_raw_buffer_load_b32(rU, offm, so, 0);
   } else if constexpr (GU == 2) {
     const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rU, offm, so, 0);
@@ -265,8 +276,9 @@ __device__ __forceinline__ void quarter(const Slot<M, GU>& s, int d, const uint3
 // sum over one tile of (s_M u_M + lo_M) x, i.e. Eq. 10 summed per group.
 // xl: the tile's 64 x pairs in LDS, read one quarter ahead of use, followed
 // by the tile's per-group sum(x) (xl[64 + gi]).
-template <int M, int GU>
-__device__ __forceinline__ float tile_partial(const Slot<M, GU>& s, const uint32_t* xl, float part) {
+template <int M, int GU, bool CB>
+__device__ __forceinline__ float tile_partial(const Slot<M, GU>& s, const uint32_t* xl, float part,
+                                              const uint32_t* tab) {
   constexpr float kM = float((1 << (M - 2)) - 1) / float(1 << (M - 1));  // (2^(M-2)-1)/2^(M-1)
   constexpr int kAcc = M == 2 ? 5 : (M >= 5 ? 3 : 2);
   float acc[GU][kAcc];
@@ -313,7 +325,9 @@ __device__ __forceinline__ float tile_partial(const Slot<M, GU>& s, const uint32
       q = acc[gi][0] * 0x1p22f + acc[gi][1] * 0x1p18f + acc[gi][2] * 0x1p14f;
     else
       q = acc[gi][0] * 0x1p22f + acc[gi][1] * 0x1p18f;
-    const float lo = h2f(s.meta[gi] & 0xffffu), st = h2f(s.meta[gi] >> 16);
+    // the group's pair: stored, or selected by its codebook index (CB)
+    const uint32_t mw = CB ? tab[(s.meta[0] >> (8 * gi)) & 0xffu] : s.meta[gi];
+    const float lo = h2f(mw & 0xffffu), st = h2f(mw >> 16);
     // s (sum u_M x) + lo_M sum(x), lo_M = lo - k_M s (Eq. 10); k_2 = 0
     const float loM = M == 2 ? lo : __builtin_fmaf(-kM, st, lo);
     part = __builtin_fmaf(st, q, part);
@@ -460,8 +474,10 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
 // of the workgroup (SIDE = 1, for grids with several workgroups per CU, where
 // its latency hides behind other workgroups) or by all waves after the main
 // loop (SIDE = 0).  SC: x is multiplied by the per-channel inverse AWQ scale
-// p.xsc as it is staged (each product rounded once to fp16).
-template <int M, int GU, int D, int SIDE, bool SC>
+// p.xsc as it is staged (each product rounded once to fp16).  CB: the group
+// metadata is a codebook index per group; each wave keeps its own LDS copy of
+// the 256 pairs (1 KB) and looks the pair up once per group.
+template <int M, int GU, int D, int SIDE, bool SC, bool CB>
 __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
   uint32_t* xs = reinterpret_cast<uint32_t*>(lds);            // x pairs, tile t at t * kXPitch
@@ -492,7 +508,8 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   const int q0 = (w * Q) / p.S, nq = ((w + 1) * Q) / p.S - q0;
   // the wave's first unit, and the lane's voffsets in a unit
   const uint32_t uo0 = uint32_t(blk * Q + q0) * p.unit_bytes;
-  const uint32_t vW = 256u * GU + 16u * uint32_t(lane), vM = 4u * GU * uint32_t(lane);
+  const uint32_t vW = p.unit_meta + 16u * uint32_t(lane), vM = (CB ? 1u : 4u) * GU * uint32_t(lane);
+  uint32_t* tab_s = reinterpret_cast<uint32_t*>(lds + p.lds_table) + 256 * w;   // this wave's pairs (CB)
   const rsrc_t rU = mk(p.units, p.units_bytes);
   auto valid = [&](int i) { return i < nq; };   // (tile columns past the row's end are zero tiles)
 
@@ -522,7 +539,9 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   }
   __builtin_amdgcn_sched_barrier(0);
   Slot<M, GU> sl[D];
-  issue(sl[0], rU, uo0, vW, vM, valid(0));
+  u32x4 tabv;
+  if constexpr (CB) tabv = ld128(mk(p.table, 1024u), 16u * uint32_t(lane));
+  issue<M, GU, CB>(sl[0], rU, uo0, vW, vM, valid(0));
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (SIDE) {                  // this wave's x-staged flag is cleared for the side wave
     flag_s[w] = 0;
@@ -582,6 +601,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     xs[(ok && li == kCpg - 1 ? (ci >> 4) : p.T4) * kXPitch + 64 + (ci & 15) / kCpg] = __builtin_bit_cast(uint32_t, v);
   }
   if constexpr (!SIDE) rp_s[w == 0 && lane <= 16 ? lane : 17] = int32_t(rpv);
+  if constexpr (CB) *reinterpret_cast<u32x4*>(tab_s + 4 * lane) = tabv;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -595,7 +615,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   // earlier waves' later steps)
 #pragma unroll
   for (int i = 1; i < D; i++) {
-    issue(sl[i], rU, uo0 + uint32_t(i) * p.unit_bytes, vW, vM, valid(i));
+    issue<M, GU, CB>(sl[i], rU, uo0 + uint32_t(i) * p.unit_bytes, vW, vM, valid(i));
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -607,9 +627,9 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   // the row's end, where the weights are zero tiles too).
   const int xo0 = (4 * q0 + cg) * kXPitch;
   auto step = [&](Slot<M, GU>& s, int i) {
-    if (i < nq) part = tile_partial<M, GU>(s, xs + xo0 + 4 * kXPitch * i, part);
+    if (i < nq) part = tile_partial<M, GU, CB>(s, xs + xo0 + 4 * kXPitch * i, part, tab_s);
     __builtin_amdgcn_sched_barrier(0);   // reuse the slot's registers: no loads hoisted above
-    issue(s, rU, uo0 + uint32_t(i + D) * p.unit_bytes, vW, vM, valid(i + D));
+    issue<M, GU, CB>(s, rU, uo0 + uint32_t(i + D) * p.unit_bytes, vW, vM, valid(i + D));
   };
 #pragma unroll
   for (int i = 0; i < D; i++) step(sl[i], i);
@@ -797,8 +817,8 @@ constexpr int kMaxWaves = 16;   // waves per workgroup (incl. a side-record wave
 // LDS carve-up: per tile (padded tile columns, plus a spare tile) 64 dwords
 // of x and its per-group sum(x) (up to 4 dwords), per-wave lane partials, the
 // block's row_ptr (plus a spare slot), side-record run sums (17 per 64-entry
-// batch), per-wave x-staged flags.
-static size_t lds_layout(int C, int S, dev::GemvParams* prm) {
+// batch), per-wave x-staged flags, per-wave copies of the 256 codebook pairs.
+static size_t lds_layout(int C, int S, bool cb, dev::GemvParams* prm) {
   size_t o = size_t(padded_tcols(C) + 1) * dev::kXPitch * 4;
   if (prm) prm->lds_part = uint32_t(o);
   o += size_t(S) * 64 * 4;
@@ -809,6 +829,9 @@ static size_t lds_layout(int C, int S, dev::GemvParams* prm) {
   o += size_t(dev::kEntries) * S * 17 * 4;
   if (prm) prm->lds_flag = uint32_t(o);
   o += size_t(kMaxWaves) * 4;
+  o = (o + 15) & ~size_t(15);
+  if (prm) prm->lds_table = uint32_t(o);
+  if (cb) o += size_t(S) * 1024;
   return o;
 }
 
@@ -847,7 +870,7 @@ static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   c->side = side;
   c->grid = nblk;
   c->nt_max = (Q + S - 1) / S;
-  c->lds = lds_layout(h.cols, S, &c->prm);
+  c->lds = lds_layout(h.cols, S, h.codebook != 0, &c->prm);
   if (c->lds > device_lds_limit()) return false;
   c->prm.R = h.rows; c->prm.C = h.cols; c->prm.T = T; c->prm.T4 = int32_t(padded_tcols(h.cols));
   c->prm.S = S; c->prm.g = h.group;
@@ -856,15 +879,16 @@ static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
 
 template <int M, int GU, int D>
 static hipError_t launch_gemv(const LaunchCfg& c, hipStream_t st) {
-  const bool sc = c.prm.xsc != nullptr;
-  if (c.side && sc)
-    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 1, true>), dim3(c.grid), dim3(64 * (c.S + 1)), c.lds, st, c.prm);
-  else if (c.side)
-    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 1, false>), dim3(c.grid), dim3(64 * (c.S + 1)), c.lds, st, c.prm);
-  else if (sc)
-    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 0, true>), dim3(c.grid), dim3(64 * c.S), c.lds, st, c.prm);
-  else
-    hipLaunchKernelGGL((dev::gemv_kernel<M, GU, D, 0, false>), dim3(c.grid), dim3(64 * c.S), c.lds, st, c.prm);
+  const bool sc = c.prm.xsc != nullptr, cb = c.prm.table != nullptr;
+  const dim3 grid(c.grid), block(64 * (c.S + (c.side ? 1 : 0)));
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, c.lds, st, c.prm); };
+  if (c.side) {
+    if (cb) sc ? go(dev::gemv_kernel<M, GU, D, 1, true, true>) : go(dev::gemv_kernel<M, GU, D, 1, false, true>);
+    else sc ? go(dev::gemv_kernel<M, GU, D, 1, true, false>) : go(dev::gemv_kernel<M, GU, D, 1, false, false>);
+  } else {
+    if (cb) sc ? go(dev::gemv_kernel<M, GU, D, 0, true, true>) : go(dev::gemv_kernel<M, GU, D, 0, false, true>);
+    else sc ? go(dev::gemv_kernel<M, GU, D, 0, true, false>) : go(dev::gemv_kernel<M, GU, D, 0, false, false>);
+  }
   return hipGetLastError();
 }
 
@@ -938,6 +962,7 @@ int stagq_query(stagq_handle h, stagq_info* out) {
   memset(out, 0, sizeof(*out));
   out->rows = h->hdr.rows; out->cols = h->hdr.cols; out->group = h->hdr.group;
   out->nbits_max = h->hdr.nbits; out->nnz = h->hdr.nnz; out->image_bytes = h->hdr.total;
+  out->codebook = h->hdr.codebook;
   for (int b = 2; b <= h->hdr.nbits; b++) out->bytes_read[b] = bytes_read(h->hdr, b);
   return STAGQ_OK;
 }
@@ -959,6 +984,8 @@ static int gemv_call(stagq_handle h, const void* x, const void* x_scale, bool sc
   if (!plan_gemv(H, bits, &c)) return STAGQ_ESHAPE;
   const uint8_t* b = h->dev;
   c.prm.units = b + H.off_units;
+  c.prm.table = H.codebook ? reinterpret_cast<const uint32_t*>(b + H.off_table) : nullptr;
+  c.prm.unit_meta = uint32_t(H.unit_meta_bytes);
   c.prm.row_ptr = b + H.off_rowptr;
   c.prm.side = b + H.off_side;
   c.prm.x = static_cast<const uint32_t*>(x);

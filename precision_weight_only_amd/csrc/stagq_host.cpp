@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdlib>
 #include <thread>
@@ -50,11 +51,34 @@ uint16_t double_to_half(double v) {
 static bool half_finite(uint16_t h) { return ((h >> 10) & 31) != 31; }
 
 // ------------------------------------------------------------- validate ----
+// The 256 pairs (lo | s << 16) codebook metadata selects: index i * 16 + j
+// has s = fp16(2^log2s[i]) and lo = fp16(ratio[j] * s), each from float64
+// and rounded once to nearest even.
+void codebook_pairs(const stagq_codebook* cb, uint32_t* out) {
+  for (int i = 0; i < 16; i++) {
+    const uint16_t s16 = double_to_half(std::exp2(half_to_double(cb->log2s[i])));
+    for (int j = 0; j < 16; j++) {
+      const uint16_t lo16 = double_to_half(half_to_double(cb->ratio[j]) * half_to_double(s16));
+      out[i * 16 + j] = uint32_t(lo16) | (uint32_t(s16) << 16);
+    }
+  }
+}
+
 int validate_fields(const stagq_fields* f, ImageHeader* h) {
   if (!f) return STAGQ_EINVAL;
-  if (!layout(f->rows, f->cols, f->group, f->nbits_max, f->nnz, h)) return STAGQ_ESHAPE;
+  const stagq_codebook* cb = f->codebook;
+  if (!layout(f->rows, f->cols, f->group, f->nbits_max, f->nnz, h, cb != nullptr)) return STAGQ_ESHAPE;
   const int64_t R = f->rows, C = f->cols, G = C / f->group, N = f->nbits_max;
   if (R > 0 && (!f->q || !f->lo || !f->s || (N > 2 && !f->planes))) return STAGQ_EINVAL;
+  if (cb) {
+    if (!cb->log2s || !cb->ratio || (R > 0 && !cb->idx)) return STAGQ_EINVAL;
+    for (int i = 0; i < 16; i++)
+      if (!half_finite(cb->log2s[i]) || !half_finite(cb->ratio[i])) return STAGQ_EFIELD;
+    uint32_t tab[256];
+    codebook_pairs(cb, tab);
+    for (int64_t i = 0; i < R * G; i++)      // lo, s must be the pairs the indices select
+      if (tab[cb->idx[i]] != (uint32_t(f->lo[i]) | (uint32_t(f->s[i]) << 16))) return STAGQ_EFIELD;
+  }
   if (!f->row_ptr) return STAGQ_EINVAL;
   if (f->nnz > 0 && (!f->col || !f->val)) return STAGQ_EINVAL;
   const int64_t n = R * C;
@@ -85,8 +109,10 @@ int validate_fields(const stagq_fields* f, ImageHeader* h) {
 // 64-row block are not counted.
 uint64_t bytes_read(const ImageHeader& h, int bits) {
   const uint64_t n = uint64_t(h.rows) * h.cols;
-  return n * 2 / 8 + n * uint64_t(bits - 2) / 8 + uint64_t(h.rows) * (h.cols / h.group) * 4 +
-         uint64_t(h.rows + 1) * 4 + uint64_t(h.nnz) * 8 + uint64_t(h.cols) * 2 + uint64_t(h.rows) * 4;
+  const uint64_t meta = h.codebook ? uint64_t(h.rows) * (h.cols / h.group) + 1024
+                                   : uint64_t(h.rows) * (h.cols / h.group) * 4;
+  return n * 2 / 8 + n * uint64_t(bits - 2) / 8 + meta + uint64_t(h.rows + 1) * 4 + uint64_t(h.nnz) * 8 +
+         uint64_t(h.cols) * 2 + uint64_t(h.rows) * 4;
 }
 
 // ----------------------------------------------------------------- pack ----
@@ -113,7 +139,10 @@ static void pack_rows(const stagq_fields* f, const ImageHeader& h, uint8_t* img,
       }
       for (int gi = 0; gi < GU; gi++) {
         const int64_t gidx = r * G + t * GU + gi;
-        put(uo + unit_pair(h, sl, gi), uint32_t(f->lo[gidx]) | (uint32_t(f->s[gidx]) << 16));
+        if (f->codebook)
+          img[uo + unit_pair(h, sl, gi)] = f->codebook->idx[gidx];
+        else
+          put(uo + unit_pair(h, sl, gi), uint32_t(f->lo[gidx]) | (uint32_t(f->s[gidx]) << 16));
       }
     }
 }
@@ -159,7 +188,7 @@ const char* stagq_strerror(int status) {
 size_t stagq_packed_bytes(const stagq_fields* f) {
   if (!f) return 0;
   ImageHeader h;
-  if (!layout(f->rows, f->cols, f->group, f->nbits_max, f->nnz, &h)) return 0;
+  if (!layout(f->rows, f->cols, f->group, f->nbits_max, f->nnz, &h, f->codebook != nullptr)) return 0;
   return size_t(h.total);
 }
 
@@ -173,6 +202,7 @@ int stagq_pack_host(const stagq_fields* f, void* dst, size_t dst_bytes) {
   uint8_t* img = static_cast<uint8_t*>(dst);
   memset(img, 0, size_t(h.total));
   memcpy(img, &h, sizeof(h));
+  if (f->codebook) codebook_pairs(f->codebook, reinterpret_cast<uint32_t*>(img + h.off_table));
   parallel_for(f->rows, [&](int64_t a, int64_t b) { pack_rows(f, h, img, a, b); });
   const int64_t R = f->rows, G = f->cols / f->group;
   memcpy(img + h.off_rowptr, f->row_ptr, size_t(R + 1) * 4);
@@ -204,12 +234,12 @@ int stagq_unpack_host(const void* image, size_t image_bytes, stagq_info* shape, 
   memcpy(&h, image, sizeof(h));
   if (h.magic != kImageMagic || h.version != kImageVersion) return STAGQ_EIMAGE;
   ImageHeader chk;
-  if (!layout(h.rows, h.cols, h.group, h.nbits, h.nnz, &chk) || chk.total != h.total)
+  if (!layout(h.rows, h.cols, h.group, h.nbits, h.nnz, &chk, h.codebook != 0) || chk.total != h.total)
     return STAGQ_EIMAGE;
   if (image_bytes < h.total) return STAGQ_ESIZE;
   memset(shape, 0, sizeof(*shape));
   shape->rows = h.rows; shape->cols = h.cols; shape->group = h.group; shape->nbits_max = h.nbits;
-  shape->nnz = h.nnz; shape->image_bytes = h.total;
+  shape->nnz = h.nnz; shape->image_bytes = h.total; shape->codebook = h.codebook;
   for (int b = 2; b <= h.nbits; b++) shape->bytes_read[b] = bytes_read(h, b);
   const uint8_t* img = static_cast<const uint8_t*>(image);
   const int64_t R = h.rows, C = h.cols, T = C / kTileCols, n = R * C;
@@ -229,7 +259,8 @@ int stagq_unpack_host(const void* image, size_t image_bytes, stagq_info* shape, 
                 uint8_t((get(uo + unit_plane_dword(h, k, sl, c >> 5)) >> col_plane_bit(c)) & 1);
       }
       for (int gi = 0; gi < GU; gi++) {
-        const uint32_t mw = get(uo + unit_pair(h, sl, gi));
+        const uint32_t mw = h.codebook ? get(h.off_table + 4 * uint64_t(img[uo + unit_pair(h, sl, gi)]))
+                                       : get(uo + unit_pair(h, sl, gi));
         if (lo) lo[r * G + t * GU + gi] = uint16_t(mw & 0xffff);
         if (s) s[r * G + t * GU + gi] = uint16_t(mw >> 16);
       }

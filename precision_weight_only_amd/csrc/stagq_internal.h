@@ -18,6 +18,9 @@ namespace stagq {
 double half_to_double(uint16_t h);
 uint16_t double_to_half(double v);
 
+// The 256 pairs (lo | s << 16) of codebook metadata, by index i * 16 + j.
+void codebook_pairs(const stagq_codebook* cb, uint32_t* out);
+
 // Validate a field set against its layout; returns STAGQ_OK or a status.
 int validate_fields(const stagq_fields* f, ImageHeader* h);
 

@@ -12,16 +12,18 @@
 //   unit (r / 16, c / 4)
 //
 // Inside a unit, in this order (the prefix property of the StagQ main stream,
-// section 3.3: a read at precision M touches the first 256 g' + 1024 M bytes
-// of every unit, never the deeper planes; g' = 128 / g groups per tile):
+// section 3.3: a read at precision M touches the first m + 1024 M bytes of
+// every unit, never the deeper planes; g' = 128 / g groups per tile):
 //
-//   group pairs    64 slots x g' x 4 B   (fp16 lo | fp16 s << 16 per group)
+//   group metadata 64 slots x g' x 4 B   (fp16 lo | fp16 s << 16 per group), or
+//                  64 slots x g' x 1 B   (codebook index per group; m = 64 g')
 //   base, chunk 0  64 slots x 16 B       (dwords 0..3 of the 32-byte base tile)
 //   base, chunk 1  64 slots x 16 B       (dwords 4..7)
 //   plane k        64 slots x 16 B       for k = 3..N (1 bit per weight)
 //
-// so one wave step reads one contiguous piece of 256 g' + 1024 M bytes.
-// After the units:
+// so one wave step reads one contiguous piece of m + 1024 M bytes.  With
+// codebook metadata the 256 (lo | s << 16) pairs the indices select sit
+// before the units (1 KB).  After the units:
 //
 //   row_ptr        [rows + 1] int32              (side record, CSR by row)
 //   side entries   one u64 per held-out weight, in (row, col) order:
@@ -59,10 +61,11 @@ struct ImageHeader {           // first 256 bytes of an image
   int64_t nnz;
   int64_t tiles;               // U = padded rows * T4
   int32_t rows_padded, blocks; // rows rounded up to 16, and their 16-row blocks
-  int32_t quads, pad0;         // Q = T4 / 4 units per block
-  uint64_t off_units, unit_bytes, unit_meta_bytes;  // unit array; bytes per unit; pairs per unit
+  int32_t quads, codebook;     // Q = T4 / 4 units per block; 1 = codebook metadata
+  uint64_t off_units, unit_bytes, unit_meta_bytes;  // unit array; bytes per unit; metadata per unit
   uint64_t off_rowptr, off_side, off_sideval, total;
-  uint64_t pad[18];
+  uint64_t off_table;          // codebook metadata: the 256 pairs (0 otherwise)
+  uint64_t pad[17];
 };
 static_assert(sizeof(ImageHeader) == 256, "image header is 256 bytes");
 
@@ -83,10 +86,11 @@ inline uint64_t unit_offset(const ImageHeader& h, int64_t row, int64_t tcol) {
   return h.off_units + uint64_t((row / kBlockRows) * h.quads + tcol / 4) * h.unit_bytes;
 }
 inline int unit_slot(int64_t row, int64_t tcol) { return int((tcol % 4) * kBlockRows + row % kBlockRows); }
-// Offsets inside a unit: pair gi of slot t; base dword dw (0..7) of slot t;
-// dword d (0..3) of plane k (3..N) of slot t.
+// Offsets inside a unit: metadata of group gi of slot t (its pair, or its
+// codebook index byte); base dword dw (0..7) of slot t; dword d (0..3) of
+// plane k (3..N) of slot t.
 inline uint64_t unit_pair(const ImageHeader& h, int t, int gi) {
-  return uint64_t(t) * (h.unit_meta_bytes / kUnitTiles) + uint64_t(gi) * 4;
+  return uint64_t(t) * (h.unit_meta_bytes / kUnitTiles) + uint64_t(gi) * (h.codebook ? 1 : 4);
 }
 inline uint64_t unit_base_dword(const ImageHeader& h, int t, int dw) {
   return h.unit_meta_bytes + uint64_t(dw >> 2) * kChunkStride + uint64_t(t) * 16 + uint64_t(dw & 3) * 4;
@@ -98,7 +102,7 @@ inline uint64_t unit_plane_dword(const ImageHeader& h, int k, int t, int d) {
 // Fill in every size and offset of an image; returns false for an unsupported
 // shape (the caller maps that to STAGQ_ESHAPE).
 inline bool layout(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int64_t nnz,
-                   ImageHeader* h) {
+                   ImageHeader* h, bool codebook = false) {
   if (rows < 0 || rows > (1 << 30) || cols <= 0 || cols % kTileCols != 0 || cols > kMaxCols)
     return false;
   if (group != 32 && group != 64 && group != 128) return false;
@@ -112,12 +116,14 @@ inline bool layout(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int
   h->rows_padded = h->blocks * kBlockRows;
   h->tiles = int64_t(h->rows_padded) * padded_tcols(cols);
   h->quads = int32_t(padded_tcols(cols) / 4);
-  h->unit_meta_bytes = uint64_t(kUnitTiles) * (kTileCols / group) * 4;
+  h->codebook = codebook ? 1 : 0;
+  h->unit_meta_bytes = uint64_t(kUnitTiles) * (kTileCols / group) * (codebook ? 1 : 4);
   h->unit_bytes = h->unit_meta_bytes + uint64_t(nbits) * kChunkStride;
   const uint64_t units = uint64_t(h->blocks) * h->quads;
   // One buffer resource covers the units (offsets below 2^31).
   if (units * h->unit_bytes >= (uint64_t(1) << 31)) return false;
   uint64_t o = 256;
+  if (codebook) { h->off_table = o; o += 1024; }
   h->off_units = o;   o = align256(o + units * h->unit_bytes);
   h->off_rowptr = o;  o = align256(o + uint64_t(rows + 1) * 4);
   h->off_side = o;    o = align256(o + uint64_t(nnz) * 8);

@@ -328,3 +328,28 @@ def test_awq_scaled_gemv(pwo, side, monkeypatch):
                 assert np.array_equal(m.gemv(xd, M, x_scale=ad).cpu().numpy(), y)
                 monkeypatch.delenv("STAGQ_FLAG_SPINS")
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("side", ["0", "1"])
+def test_codebook_metadata_gemv(pwo, side, monkeypatch):
+    """The pages' metadata (one codebook index per group, 256 pairs per matrix;
+    the oracle's codebook encoder) against the oracle: codes bit-exact, y to the
+    parity bar, in both side-record modes, on ragged rows, g = 32 / 64 / 128,
+    N = 4 and 6; also with the run-time AWQ scale."""
+    monkeypatch.setenv("STAGQ_SIDE", side)
+    rng = np.random.default_rng(31)
+    for case in ((1001, 384, 64, 4, 0.01, "student_t", 2), (77, 640, 32, 6, 0.02, "normal_outliers", 3),
+                 (512, 2048, 128, 4, 0.001, "student_t", 4)):
+        R, Cc, g, N, frac, dist, seed = case
+        w, x = synth_matrix(R, Cc, dist, seed)
+        F = oracle.encode(w, g, N, frac, pair_fit="codebook")
+        m, xd = _check(pwo, F, x, range(2, N + 1), f"codebook {case} side={side}")
+        assert m.codebook
+        a = rng.uniform(0.5, 2.0, Cc).astype(np.float16)
+        ad = _to_dev(a)
+        for M in (2, N):
+            _say(f"codebook {case} side={side} awq", f"bits={M}")
+            y = m.gemv(xd, M, x_scale=ad).cpu().numpy()
+            ref = oracle.gemv_scaled(F, x, a, M)
+            assert _rel(y, ref) <= REL_L2_CONTRACT
+            assert _regression_ok(y, ref, F, oracle.scale_x(x, a), M)

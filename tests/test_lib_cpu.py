@@ -185,3 +185,47 @@ def test_stream_read_argument_errors():
     assert lib.stagq_stream_read(C.c_void_p(4096), 1 << 31, sink, None) == -1
     assert lib.stagq_stream_read(C.c_void_p(4104), 4096, sink, None) == -5  # EALIGN
     assert lib.stagq_stream_read(C.c_void_p(4096), 0, sink, None) == 0       # nothing to read
+
+
+def test_codebook_metadata_pack_roundtrip_and_bytes():
+    """Codebook metadata (the oracle's codebook encoder): the image stores one
+    index byte per group plus the 256 pairs once; unpacking gives back the
+    pairs the indices select, bit for bit; the GEMV's byte count charges 1 byte
+    per group + 1 KB instead of 4 bytes per group."""
+    w, _ = synth_matrix(48, 512, "student_t", 8)
+    F = oracle.encode(w, 64, 5, 0.01, pair_fit="codebook")
+    Fp = oracle.encode(w, 64, 5, 0.01)
+    img = pwo.pack_host(F)
+    U = pwo.unpack_host(img)
+    assert U["codebook"] == 1
+    for k in ("q", "planes", "row_ptr", "col"):
+        assert np.array_equal(getattr(F, k), U[k]), k
+    for k in ("lo", "s", "val"):
+        assert np.array_equal(getattr(F, k).view(np.uint16), U[k].view(np.uint16)), k
+    info, infop = _lib.Info(), _lib.Info()
+    pwo.lib().stagq_unpack_host(img.ctypes.data_as(C.c_void_p), img.size, C.byref(info),
+                                None, None, None, None, None, None, None)
+    imgp = pwo.pack_host(Fp)
+    pwo.lib().stagq_unpack_host(imgp.ctypes.data_as(C.c_void_p), imgp.size, C.byref(infop),
+                                None, None, None, None, None, None, None)
+    G = 48 * 512 // 64
+    for M in range(2, 6):
+        assert info.bytes_read[M] - (F.nnz - Fp.nnz) * 8 == infop.bytes_read[M] - 3 * G + 1024
+
+
+def test_codebook_metadata_validation():
+    """lo, s must be the pairs the indices select (else STAGQ_EFIELD), and the
+    codebook pointers must be there (else STAGQ_EINVAL)."""
+    w, _ = synth_matrix(16, 256, "student_t", 9)
+    F = oracle.encode(w, 128, 4, 0.0, pair_fit="codebook")
+    bad = oracle.Fields(**{**F.__dict__})
+    bad.idx = F.idx.copy()
+    bad.idx[0, 0] ^= 1
+    with pytest.raises(pwo.StagQError) as e:
+        pwo.pack_host(bad)
+    assert e.value.status == -7
+    bad = oracle.Fields(**{**F.__dict__})
+    bad.cb_ratio = np.zeros(0, np.float16)              # a NULL codebook
+    with pytest.raises(pwo.StagQError) as e:
+        pwo.pack_host(bad)
+    assert e.value.status == -1
