@@ -112,6 +112,29 @@ def graph_time(launch, n_copies, K, bits_seq):
     return e0.elapsed_time(e1) * 1e3 / K
 
 
+def codebook_fields(fields):
+    """Timing workload for codebook metadata at full size: two uniform 16-entry
+    codebooks over the range of the encoder's pairs (log2 s and lo/s) and per
+    group the nearest index; lo, s become the pairs the indices select.  (The
+    per-group Eq. 5 choice is the oracle's and is parity-tested on smaller
+    shapes; the GEMV's cost does not depend on which index a group holds.)"""
+    lo = fields["lo"].astype(np.float64)
+    s = fields["s"].astype(np.float64)
+    pos = s > 0
+    L, P = np.log2(s[pos]), lo[pos] / s[pos]
+    t = np.arange(16) / 15.0
+    cs = (L.min() + t * (L.max() - L.min())).astype(np.float16)
+    cr = (P.min() + t * (P.max() - P.min())).astype(np.float16)
+    ts = np.exp2(cs.astype(np.float64)).astype(np.float16)
+    i = np.abs(np.log2(np.where(pos, s, 1.0))[..., None] - cs.astype(np.float64)).argmin(-1)
+    sv = ts[i].astype(np.float64)
+    j = np.abs((lo / sv)[..., None] - cr.astype(np.float64)).argmin(-1)
+    out = dict(fields)
+    out.update(idx=(i * 16 + j).astype(np.uint8), cb_log2s=cs, cb_ratio=cr, s=ts[i],
+               lo=(cr.astype(np.float64)[j] * sv).astype(np.float16))
+    return out
+
+
 def read_ceiling(bytes_alg, args):
     """Streaming-read ceiling per precision: a plain read of the same byte
     count (stagq_stream_read), K launches in one graph cycling through fresh
@@ -157,6 +180,7 @@ def sweep(args):
             fields = pwo.encode(w, wl.group, wl.nbits, K, wl.ratio_T)
             del w
             base = pwo.StagQMatrix.pack(fields, device=dev)
+            cbm = pwo.StagQMatrix.pack(codebook_fields(fields), device=dev) if wname == "mlp" else None
             del fields
             n_copies = max(2, -(-args.rot_mb * (1 << 20) // base.bytes_read[min(wl.bits)]))
             copies = [base] + [base.replicate() for _ in range(n_copies - 1)]
@@ -187,6 +211,18 @@ def sweep(args):
                 for M in wl.bits:
                     us = graph_time(launch_sc, n_copies, args.steps, [M])
                     entry["bits"][str(M)]["awq_scaled_us"] = round(us, 3)
+                # the same GEMVs on codebook metadata (1 byte per group + 256 pairs)
+                cbc = [cbm] + [cbm.replicate() for _ in range(n_copies - 1)]
+
+                def launch_cb(c, M):
+                    cbc[c].gemv(xd, M, y=ys[c])
+
+                for M in wl.bits:
+                    us = graph_time(launch_cb, n_copies, args.steps, [M])
+                    b = cbm.bytes_read[M]
+                    entry["bits"][str(M)]["codebook"] = {"us": round(us, 3), "bytes": int(b),
+                                                         "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2)}
+                del cbc, cbm
             if wname == "layer_sweep":
                 us = graph_time(launch, n_copies, args.steps, list(wl.bits))
                 b = sum(base.bytes_read[M] for M in wl.bits) / len(wl.bits)
@@ -194,7 +230,8 @@ def sweep(args):
             rows.append(entry)
             print(f"[sweep] {wname}/{mat.name} {mat.rows}x{mat.cols}: " +
                   " ".join(f"{M}b {v['us']}us {v['pct_peak']}%" +
-                           (f" (awq {v['awq_scaled_us']}us)" if "awq_scaled_us" in v else "")
+                           (f" (awq {v['awq_scaled_us']}us)" if "awq_scaled_us" in v else "") +
+                           (f" (codebook {v['codebook']['us']}us)" if "codebook" in v else "")
                            for M, v in entry["bits"].items()),
                   file=sys.stderr, flush=True)
             del copies, base, ys
