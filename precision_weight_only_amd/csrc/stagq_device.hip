@@ -6,12 +6,14 @@
 //    second pass).  A wave step covers 16 rows x 4 consecutive tile columns:
 //    lane = (tile column within the four) * 16 + row.  The S waves of the
 //    workgroup split the row's groups of four tile columns between them.
-//  * Per step a wave issues one contiguous 1 KB dwordx4 load per stream chunk
-//    (base stream, planes 3..M) and one load of the group pairs, D steps ahead
-//    of use: step 0 before the wave stages its x, steps 1..D-1 right after
-//    (so across the chip every wave's first step is requested before anyone's
-//    second).  All global loads of the streams go through buffer resources:
-//    out-of-range offsets read zeros instead of faulting.
+//  * The 64 tiles of a wave step are one contiguous unit of the image (group
+//    metadata, base chunks 0-1, planes 3..N): per step a wave reads the first
+//    m + 1024 M bytes of its unit (one dwordx4 load per 1 KB chunk stretch and
+//    one load of its metadata), D steps ahead of use: step 0 before the wave
+//    stages its x, steps 1..D-1 right after (so across the chip every wave's
+//    first step is requested before anyone's second).  All global loads go
+//    through buffer resources: out-of-range offsets read zeros instead of
+//    faulting.
 //  * Each wave stages the x of its own tile columns in LDS (68 dwords per
 //    tile: 64 of x, so the four tile columns of a step fall in different
 //    banks, then the tile's sum(x) per group); a step reads its tile's x one
@@ -23,7 +25,11 @@
 //    merged with the base codes into 4-bit codes (Eq. 8) with shifts and
 //    bit-field inserts.
 //  * Per group: s_M * sum(u x) + lo_M * sum(x) (the affine collapse of Eq. 10
-//    summed over the group), in fp32.
+//    summed over the group), in fp32; the pair (lo, s) is stored per group or,
+//    with codebook metadata, looked up by the group's index byte in an LDS
+//    copy of the matrix's 256 pairs.
+//  * Optionally x is multiplied by a per-channel inverse AWQ scale as it is
+//    staged.
 //  * Side record (Eq. 4): each entry carries a = P - lo - s (q - 1/2) and s, so
 //    its contribution (P - W_main) x_c = (a - s 2^(1-M)) x_c needs only x_c
 //    (the main stream decodes W_main = lo + s (q - 1/2 + 2^(1-M)) there because
@@ -35,6 +41,8 @@
 //  * Row sums: the 4 S lane partials of a row, then its corrections, are added
 //    in a fixed order (no atomics), so y is bitwise reproducible for a given
 //    shape and M.
+// A streaming-read kernel (the ceiling the GEMV is measured against) sits
+// beside them.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
