@@ -211,6 +211,16 @@ def sweep(args):
                 for M in wl.bits:
                     us = graph_time(launch_sc, n_copies, args.steps, [M])
                     entry["bits"][str(M)]["awq_scaled_us"] = round(us, 3)
+                # the same GEMVs with an fp16 result (stagq_gemv_f16)
+                y16 = [torch.empty(mat.rows, dtype=torch.float16, device=dev) for _ in range(n_copies)]
+
+                def launch_h(c, M):
+                    copies[c].gemv(xd, M, y=y16[c])
+
+                for M in wl.bits:
+                    us = graph_time(launch_h, n_copies, args.steps, [M])
+                    entry["bits"][str(M)]["fp16_out_us"] = round(us, 3)
+                del y16
                 # the same GEMVs on codebook metadata (1 byte per group + 256 pairs)
                 cbc = [cbm] + [cbm.replicate() for _ in range(n_copies - 1)]
 
@@ -231,6 +241,7 @@ def sweep(args):
             print(f"[sweep] {wname}/{mat.name} {mat.rows}x{mat.cols}: " +
                   " ".join(f"{M}b {v['us']}us {v['pct_peak']}%" +
                            (f" (awq {v['awq_scaled_us']}us)" if "awq_scaled_us" in v else "") +
+                           (f" (fp16 out {v['fp16_out_us']}us)" if "fp16_out_us" in v else "") +
                            (f" (codebook {v['codebook']['us']}us)" if "codebook" in v else "")
                            for M, v in entry["bits"].items()),
                   file=sys.stderr, flush=True)

@@ -171,6 +171,22 @@ int stagq_gemv_scaled(stagq_handle h, const void* x, const void* x_scale, float*
                       void* hip_stream);
 
 /*
+ * The GEMV with an fp16 result, for a consumer that takes fp16 activations:
+ * y_r = fp16(the fp32 row sum stagq_gemv or stagq_gemv_scaled would write),
+ * rounded once to nearest even in the same launch (no second pass over y);
+ * a row sum of magnitude 65520 or more becomes +-inf.
+ *   x_scale  NULL for no activation scale, else the inverse AWQ scale as in
+ *            stagq_gemv_scaled (device fp16 [cols], 16-byte aligned)
+ *   y        device, fp16 [rows], 2-byte aligned (written, not accumulated)
+ * Same launch, cost and determinism as stagq_gemv, with 2 bytes written per
+ * row instead of 4.  ([StagQ] Appendix G: the pages' kernel accumulates in
+ * half precision and adds into a half-precision output with atomics; here the
+ * sums stay fp32 in a fixed order and only the stored value is fp16.)
+ */
+int stagq_gemv_f16(stagq_handle h, const void* x, const void* x_scale, void* y, int bits,
+                   void* hip_stream);
+
+/*
  * Write the composite integers u_bits (Eq. 8) of the main stream as decoded by
  * the GEMV path: codes is device uint8 [rows*cols], row-major, 16-byte aligned.
  * Asynchronous on hip_stream.  (Held-out positions decode like any other: q

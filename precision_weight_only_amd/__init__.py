@@ -164,14 +164,22 @@ class StagQMatrix:
         buf.copy_(self.buffer)
         return self.clone_to(buf)
 
-    def gemv(self, x, bits: int, y=None, stream=None, x_scale=None):
-        """y = W_hat^(bits) x for an fp16 device vector x; returns fp32 y.
+    def gemv(self, x, bits: int, y=None, stream=None, x_scale=None, out_dtype=None):
+        """y = W_hat^(bits) x for an fp16 device vector x; returns fp32 y, or
+        fp16 y (stagq_gemv_f16) when out_dtype or the given y is torch.float16.
         x_scale: optional fp16 device vector [cols] of inverse AWQ scales, applied
         to x as it is staged (stagq_gemv_scaled)."""
         torch = _torch()
         if y is None:
-            y = torch.empty(self.rows, dtype=torch.float32, device=x.device)
-        if x_scale is None:
+            y = torch.empty(self.rows, dtype=out_dtype or torch.float32, device=x.device)
+        if y.dtype == torch.float16:
+            check(lib().stagq_gemv_f16(self._h, C.c_void_p(x.data_ptr()),
+                                       C.c_void_p(x_scale.data_ptr()) if x_scale is not None else None,
+                                       C.c_void_p(y.data_ptr()), int(bits), _stream_ptr(stream)),
+                  "stagq_gemv_f16")
+        elif y.dtype != torch.float32:
+            raise TypeError("gemv: y must be float32 or float16")
+        elif x_scale is None:
             check(lib().stagq_gemv(self._h, C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()),
                                    int(bits), _stream_ptr(stream)), "stagq_gemv")
         else:

@@ -61,6 +61,7 @@ def _load() -> C.CDLL:
         "stagq_rebind": (C.c_int, [P, P, C.c_size_t, C.POINTER(P)]),
         "stagq_gemv": (C.c_int, [P, P, P, C.c_int, P]),
         "stagq_gemv_scaled": (C.c_int, [P, P, P, P, C.c_int, P]),
+        "stagq_gemv_f16": (C.c_int, [P, P, P, P, C.c_int, P]),
         "stagq_decode_codes": (C.c_int, [P, C.c_int, P, P]),
         "stagq_query": (C.c_int, [P, C.POINTER(Info)]),
         "stagq_destroy": (None, [P]),
@@ -85,6 +86,7 @@ EXPORTED = (
     "stagq_packed_bytes", "stagq_pack_host", "stagq_pack", "stagq_rebind", "stagq_gemv",
     "stagq_decode_codes", "stagq_query", "stagq_destroy", "stagq_strerror", "stagq_encode",
     "stagq_unpack_host", "stagq_plan_gemv", "stagq_stream_read", "stagq_gemv_scaled",
+    "stagq_gemv_f16",
 )
 
 

@@ -100,6 +100,13 @@ __device__ __forceinline__ uint32_t hmul2(uint32_t a, uint32_t b) {
 __device__ __forceinline__ float h2f(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
+
+// y_r as fp32, or rounded once to fp16 (nearest even; beyond the fp16 range,
+// +-inf) when the caller asked for an fp16 result.
+__device__ __forceinline__ void store_y(float* y, uint16_t* y16, int r, float v) {
+  if (y16) y16[r] = __builtin_bit_cast(uint16_t, (_Float16)v);
+  else y[r] = v;
+}
 __device__ __forceinline__ uint64_t ld64side(rsrc_t r, uint32_t off) {
   const u32x2 v = ld64(r, off);
   return uint64_t(v[0]) | (uint64_t(v[1]) << 32);
@@ -129,6 +136,7 @@ struct GemvParams {
   const uint32_t* x;       // fp16 pairs
   const uint32_t* xsc;     // fp16 pairs: inverse AWQ scale per input channel (scaled GEMV only)
   float* y;
+  uint16_t* y16;           // fp16 result instead of y (fp16-output GEMV only)
   uint32_t unit_bytes, units_bytes, side_bytes, rp_bytes, x_bytes;
   uint32_t unit_meta;      // bytes of group metadata at the start of a unit
   int32_t R, C, T, T4, S;  // rows, cols, tiles per row (padded to a multiple of 4), waves per workgroup
@@ -659,7 +667,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   }
   if constexpr (SIDE) {
     // ... then the row's side-record total from the side-record wave.
-    if (owner && row_ok) p.y[r] = acc + runs_s[lane];
+    if (owner && row_ok) store_y(p.y, p.y16, r, acc + runs_s[lane]);
     return;
   }
 
@@ -710,7 +718,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
       for (int q = a; q < b; q = (q | 63) + 1) acc += runs_s[(q >> 6) * 17 + lane];
     }
   }
-  if (owner && row_ok) p.y[r] = acc;
+  if (owner && row_ok) store_y(p.y, p.y16, r, acc);
 }
 
 // Streaming-read ceiling: a workgroup of 256 threads reads 16 KB (4 x 16 B per
@@ -977,14 +985,14 @@ int stagq_query(stagq_handle h, stagq_info* out) {
 
 void stagq_destroy(stagq_handle h) { delete h; }
 
-static int gemv_call(stagq_handle h, const void* x, const void* x_scale, bool scaled, float* y, int bits,
-                     void* hip_stream) {
+static int gemv_call(stagq_handle h, const void* x, const void* x_scale, bool scaled, void* y, bool half,
+                     int bits, void* hip_stream) {
   if (!h) return STAGQ_EINVAL;
   const ImageHeader& H = h->hdr;
   if (bits < 2 || bits > H.nbits) return STAGQ_EBITS;
   if (H.rows == 0) return STAGQ_OK;  // nothing to compute; y may be empty
   if (!x || !y || (scaled && !x_scale)) return STAGQ_EINVAL;
-  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 4 ||
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % (half ? 2 : 4) ||
       reinterpret_cast<uintptr_t>(x_scale) % 16)
     return STAGQ_EALIGN;
   const int GU = kTileCols / H.group;
@@ -998,7 +1006,8 @@ static int gemv_call(stagq_handle h, const void* x, const void* x_scale, bool sc
   c.prm.side = b + H.off_side;
   c.prm.x = static_cast<const uint32_t*>(x);
   c.prm.xsc = scaled ? static_cast<const uint32_t*>(x_scale) : nullptr;
-  c.prm.y = y;
+  c.prm.y = half ? nullptr : static_cast<float*>(y);
+  c.prm.y16 = half ? static_cast<uint16_t*>(y) : nullptr;
   c.prm.unit_bytes = uint32_t(H.unit_bytes);
   c.prm.units_bytes = uint32_t(uint64_t(H.blocks) * H.quads * H.unit_bytes);
   c.prm.side_bytes = uint32_t(H.nnz * 8);
@@ -1019,12 +1028,17 @@ static int gemv_call(stagq_handle h, const void* x, const void* x_scale, bool sc
 }
 
 int stagq_gemv(stagq_handle h, const void* x, float* y, int bits, void* hip_stream) {
-  return gemv_call(h, x, nullptr, false, y, bits, hip_stream);
+  return gemv_call(h, x, nullptr, false, y, false, bits, hip_stream);
 }
 
 int stagq_gemv_scaled(stagq_handle h, const void* x, const void* x_scale, float* y, int bits,
                       void* hip_stream) {
-  return gemv_call(h, x, x_scale, true, y, bits, hip_stream);
+  return gemv_call(h, x, x_scale, true, y, false, bits, hip_stream);
+}
+
+int stagq_gemv_f16(stagq_handle h, const void* x, const void* x_scale, void* y, int bits,
+                   void* hip_stream) {
+  return gemv_call(h, x, x_scale, x_scale != nullptr, y, true, bits, hip_stream);
 }
 
 int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int bits,

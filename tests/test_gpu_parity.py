@@ -353,3 +353,57 @@ def test_codebook_metadata_gemv(pwo, side, monkeypatch):
             ref = oracle.gemv_scaled(F, x, a, M)
             assert _rel(y, ref) <= REL_L2_CONTRACT
             assert _regression_ok(y, ref, F, oracle.scale_x(x, a), M)
+
+
+@pytest.mark.parametrize("side", ["0", "1"])
+def test_fp16_output_gemv(pwo, side, monkeypatch):
+    """The fp16-output GEMV (stagq_gemv_f16) rounds the very row sums the fp32
+    GEMV writes: bitwise fp16(y32) with and without the AWQ scale and on
+    codebook metadata, within half an fp16 ulp plus the fp32 summation bound of
+    the oracle's y and to the parity bar; row sums beyond the fp16 range become +-inf exactly where fp16(y32)
+    does."""
+    import torch
+    monkeypatch.setenv("STAGQ_SIDE", side)
+    rng = np.random.default_rng(41)
+    for case in ((1001, 384, 64, 4, 0.01, "student_t", 2, "minmax"), (77, 640, 32, 6, 0.02, "normal_outliers", 3, "codebook"),
+                 (2048, 1024, 128, 4, 0.02, "student_t", 11, "minmax")):
+        R, Cc, g, N, frac, dist, seed, fit = case
+        w, x = synth_matrix(R, Cc, dist, seed)
+        F = oracle.encode(w, g, N, frac, pair_fit=fit)
+        m = pwo.StagQMatrix.pack(F)
+        a = rng.uniform(0.5, 2.0, Cc).astype(np.float16)
+        xd, ad = _to_dev(x), _to_dev(a)
+        for M in range(2, N + 1):
+            for sc in (None, ad):
+                _say(f"fp16 out {case} side={side} awq={sc is not None}", f"bits={M}")
+                y32 = m.gemv(xd, M, x_scale=sc).cpu().numpy()
+                y16 = m.gemv(xd, M, x_scale=sc, out_dtype=torch.float16).cpu().numpy()
+                assert y16.dtype == np.float16
+                assert np.array_equal(y16.view(np.uint16), y32.astype(np.float16).view(np.uint16))
+                xe = x if sc is None else oracle.scale_x(x, a)
+                ref = oracle.gemv(F, xe, M)
+                # per row: half an fp16 ulp of rounding plus the fp32 summation
+                # error, bounded by 1e-5 of sum |W_hat| |x| as elsewhere
+                bound = 0.5 * np.spacing(np.abs(y16)).astype(np.float64) + \
+                    REL_L2_REGRESSION * (np.abs(oracle.w_hat(F, M)) @ np.abs(xe.astype(np.float64)))
+                assert np.all(np.abs(y16.astype(np.float64) - ref) <= bound)
+                assert _rel(y16, ref) <= REL_L2_CONTRACT
+    # beyond the fp16 range: large weights and activations
+    w, x = synth_matrix(256, 1024, "student_t", 5)
+    w = (w.astype(np.float64) * 4000).astype(np.float16)
+    x = (x.astype(np.float64) * 30).astype(np.float16)
+    F = oracle.encode(w, 128, 4, 0.01)
+    m = pwo.StagQMatrix.pack(F)
+    xd = _to_dev(x)
+    for M in (2, 4):
+        _say(f"fp16 out overflow side={side}", f"bits={M}")
+        y32 = m.gemv(xd, M).cpu().numpy()
+        y16 = m.gemv(xd, M, out_dtype=torch.float16).cpu().numpy()
+        with np.errstate(over="ignore"):
+            want = y32.astype(np.float16)
+        assert np.isinf(want).any() and np.isfinite(want).any()
+        assert np.array_equal(y16.view(np.uint16), want.view(np.uint16))
+    yodd = torch.empty(F.rows + 1, dtype=torch.float16, device="cuda")
+    assert pwo.lib().stagq_gemv_f16(m._h, xd.data_ptr(), None, yodd.data_ptr() + 1, 3, None) == -5
+    assert pwo.lib().stagq_gemv_f16(m._h, xd.data_ptr(), None, yodd.data_ptr() + 2, 3, None) == 0
+    torch.cuda.synchronize()

@@ -20,7 +20,7 @@ def test_header_symbols_are_exported():
     with open(os.path.join(ROOT, "include", "stagq.h")) as f:
         text = f.read()
     code = re.sub(r"/\*.*?\*/", "", text, flags=re.S)          # drop comments
-    declared = set(re.findall(r"\b(stagq_[a-z_]+)\s*\(", code))
+    declared = set(re.findall(r"\b(stagq_[a-z0-9_]+)\s*\(", code))
     assert declared == set(_lib.EXPORTED)
     lib = pwo.lib()
     for name in declared:
