@@ -103,6 +103,8 @@ class Fields:
     idx: Optional[np.ndarray] = None       # uint8 [R, G]
     cb_log2s: Optional[np.ndarray] = None  # float16 [16]
     cb_ratio: Optional[np.ndarray] = None  # float16 [16]
+    # what the full encoder chose (codebook rules, guard counts), if it ran
+    info: Optional[dict] = None
 
     @property
     def nnz(self) -> int:
@@ -198,12 +200,14 @@ def codebook_table(cb_log2s, cb_ratio):
     return lo.reshape(256), np.repeat(s, 16)
 
 
-def pair_loss(v, lo, s, nbits: int, lam: float = 4.0):
-    """D(lo, s) of Eq. (5) with E_c = 1 over the last axis of v: the mean over
-    M = 2..N of the squared reconstruction errors plus lam times the floor
-    term of Eq. (6), rho = s sum_{k=3..N} 2^-(k-1).  lo, s broadcast against
-    v's leading axes."""
+def pair_loss(v, lo, s, nbits: int, lam: float = 4.0, E=None):
+    """D(lo, s) of Eq. (5) over the last axis of v: the mean over M = 2..N of
+    the squared reconstruction errors plus lam times the floor term of Eq. (6),
+    rho = s sum_{k=3..N} 2^-(k-1).  E: the calibration mean square E_c of each
+    entry's input channel, broadcast against v (None: E_c = 1).  lo, s
+    broadcast against v's leading axes."""
     v = np.asarray(v, dtype=np.float64)
+    wt = np.ones_like(v) if E is None else np.broadcast_to(np.asarray(E, dtype=np.float64), v.shape)
     lo = np.asarray(lo, dtype=np.float64)[..., None]
     s = np.asarray(s, dtype=np.float64)[..., None]
     d = v - lo
@@ -213,12 +217,12 @@ def pair_loss(v, lo, s, nbits: int, lam: float = 4.0):
     q = np.where(s > 0.0, q, 0.0)
     rec = lo + s * q
     rho = s * sum(2.0 ** -(k - 1) for k in range(3, nbits + 1))
-    floor = (np.maximum(np.abs(v - rec) - rho, 0.0) ** 2).sum(axis=-1)
-    err = ((v - rec) ** 2).sum(axis=-1)
+    floor = (wt * np.maximum(np.abs(v - rec) - rho, 0.0) ** 2).sum(axis=-1)
+    err = (wt * (v - rec) ** 2).sum(axis=-1)
     for k in range(3, nbits + 1):
         b = (v - rec) >= 0.0
         rec = rec + np.where(s > 0.0, (2.0 * b - 1.0) * s / 2.0 ** (k - 1), 0.0)
-        err = err + ((v - rec) ** 2).sum(axis=-1)
+        err = err + (wt * (v - rec) ** 2).sum(axis=-1)
     return err / (nbits - 1) + lam * floor
 
 

@@ -18,6 +18,13 @@ value distributions below are this project's choice:
 
 Within one matrix the draw order is fixed: W, then the outlier positions (if
 any), then x ~ N(0, 1); everything is drawn in float64 and rounded to fp16.
+
+synth_channel_energy() stands in for the calibration mean square E_c of each
+input channel, which the paper measures on C4 text (not available here): a
+log-normal spread, E_c = exp(z), z ~ N(0, 1), with round(0.005 * C) channels
+(at least one) drawn without replacement and scaled by 100, the few
+large-activation channels such models show.  It has its own generator, so it
+leaves the W and x draws unchanged.
 """
 from __future__ import annotations
 
@@ -27,7 +34,7 @@ from typing import Tuple
 
 import numpy as np
 
-__all__ = ["Matrix", "Workload", "WORKLOADS", "synth_matrix", "array_digest"]
+__all__ = ["Matrix", "Workload", "WORKLOADS", "synth_matrix", "synth_channel_energy", "array_digest"]
 
 
 @dataclass(frozen=True)
@@ -96,6 +103,15 @@ def synth_matrix(rows: int, cols: int, dist: str, seed: int):
     w = _draw_w(rng, rows, cols, dist).astype(np.float16)
     x = rng.standard_normal(cols).astype(np.float16)
     return w, x
+
+
+def synth_channel_energy(cols: int, seed: int) -> np.ndarray:
+    """E_c > 0 for every input channel (float64 [cols]), drawn as described above."""
+    rng = np.random.default_rng([seed, 7])
+    e = np.exp(rng.standard_normal(cols))
+    n_big = max(1, int(np.floor(0.005 * cols + 0.5)))
+    e[rng.choice(cols, size=n_big, replace=False)] *= 100.0
+    return e
 
 
 def array_digest(a: np.ndarray) -> str:
