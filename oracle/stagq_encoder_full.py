@@ -18,42 +18,42 @@ the calibration mean square of each input channel.
 
 Readings (where the paper is silent or leaves a choice open)
 ------------------------------------------------------------
-F1  E_c is given per input channel (the tests draw a synthetic, seeded one);
+FE1  E_c is given per input channel (the tests draw a synthetic, seeded one);
     E = None means E_c = 1.  Every error below is weighted by E_c, as Eq. (5)
     and Eq. (6) weight theirs.
-F2  The codebooks are placed over log2 s0 and lo0 / s0 of the initial pairs
+FE2  The codebooks are placed over log2 s0 and lo0 / s0 of the initial pairs
     (Appendix B) of the groups with s0 > 0, the pre-grid entries clipped.
     Lloyd's rule is the unweighted one-dimensional k-means with 16 centres,
     started from the uniform placement; a value goes to its nearest centre (the
     lower one on ties), a centre moves to the mean of its values (an empty cell
     keeps its centre), and it stops when no centre moves (at most 200 rounds).
     The anchored rule keeps the first and last centres at the ends of the range.
-F3  The rule pair is chosen by the first term of Eq. (5) summed over the
+FE3  The rule pair is chosen by the first term of Eq. (5) summed over the
     matrix, each group taking its best pair under that term alone; the nine
     combinations are tried with the log2 s rule outer, in the order uniform,
     Lloyd, anchored Lloyd, and a later one must be strictly better to win.
-F4  The fallback compares errors summed over the matrix (E_c-weighted, final
+FE4  The fallback compares errors summed over the matrix (E_c-weighted, final
     per-group choice): the "six-bit error" is that of the six-bit prefix
     reconstruction, the plane rule carried to plane 6 even where fewer planes
     are stored; above a tenth of the two-bit error, both codebooks revert to
     uniform placement and every group picks again.
-F5  Gain criterion: a group's candidate is its largest-|w| entry (lowest column
+FE5  Gain criterion: a group's candidate is its largest-|w| entry (lowest column
     on ties), clipped to the nearest other value of the group toward the inside
     (the largest of the others if it is the group maximum, else the smallest).
     Scoring re-picks that group's pair among the 256 of codebooks placed
     uniformly over the unclipped initial pairs; the codebooks are not refitted
     per candidate.  D2(V) = sum_c E_c (v_c - (lo + s q_c))^2 over the values of
     its argument, with the pair the Eq. (5) choice makes for them.
-F6  The bits a pre-grid entry occupies are b = 8 + log2(n / k) + log2 e
+FE6  The bits a pre-grid entry occupies are b = 8 + log2(n / k) + log2 e
     (Appendix E's 8-bit code and position charge, n weights, k held out), with
     k solved by a fixed-point iteration that starts from the number of
     positive gains (k can only fall, so it settles).
-F7  Post-grid guard over the entries the pre-grid guard left: under the ratio
+FE7  Post-grid guard over the entries the pre-grid guard left: under the ratio
     criterion exactly one entry per row, the largest E_c (w - (lo + s q))^2
     (lowest column on ties); under the gain criterion that error per stored
     bit, b_post = 16 + ceil(log2 C) (an fp16 residual and a column index), the
     three highest of each row kept when above tau.
-F8  The side record stores the held-out weight itself as fp16 (reading R6 of
+FE8  The side record stores the held-out weight itself as fp16 (reading R6 of
     the main oracle module); the paper's 8-bit codes and fp16 residuals change
     only how P is stored and are not modelled.  Neither guard has a budget cap.
 
@@ -79,7 +79,7 @@ RULES = ("uniform", "lloyd", "lloyd_anchored")
 
 
 def lloyd_1d(values, init, anchored: bool = False, max_iter: int = 200) -> np.ndarray:
-    """Lloyd's rule on the real line (reading F2): alternate nearest-centre
+    """Lloyd's rule on the real line (reading FE2): alternate nearest-centre
     assignment (lower centre on ties) and centre = mean of its cell; anchored
     keeps the first and last centres where init put them."""
     v = np.asarray(values, dtype=np.float64).ravel()
@@ -137,7 +137,7 @@ def _base_code(v, lo, s):
 
 
 def two_bit_error(v, E, lo, s) -> np.ndarray:
-    """D2 = sum_c E_c (v_c - (lo + s q_c))^2 over the last axis (reading F5)."""
+    """D2 = sum_c E_c (v_c - (lo + s q_c))^2 over the last axis (reading FE5)."""
     v = np.asarray(v, dtype=np.float64)
     wt = np.broadcast_to(np.asarray(E, dtype=np.float64), v.shape)
     lo = np.asarray(lo, dtype=np.float64)[..., None]
@@ -146,7 +146,7 @@ def two_bit_error(v, E, lo, s) -> np.ndarray:
 
 
 def _prefix_error(v, E, lo, s, M: int) -> float:
-    """sum E_c (v - W^(M))^2 with the plane rule carried to plane M (F4)."""
+    """sum E_c (v - W^(M))^2 with the plane rule carried to plane M (FE4)."""
     lo = lo[..., None]
     s = s[..., None]
     rec = lo + s * _base_code(v, lo, s)
@@ -157,7 +157,7 @@ def _prefix_error(v, E, lo, s, M: int) -> float:
 
 
 def clip_candidate(g: np.ndarray) -> Tuple[int, np.ndarray]:
-    """The gain criterion's candidate in one group (reading F5): its position
+    """The gain criterion's candidate in one group (reading FE5): its position
     and the group's values with it clipped to the next value inward."""
     g = np.asarray(g, dtype=np.float64)
     j = int(np.argmax(np.abs(g)))
@@ -169,18 +169,18 @@ def clip_candidate(g: np.ndarray) -> Tuple[int, np.ndarray]:
 
 
 def entry_bits(n: int, k: int) -> float:
-    """Bits of one pre-grid entry under the gain criterion (F6)."""
+    """Bits of one pre-grid entry under the gain criterion (FE6)."""
     return 8.0 + math.log2(n / k) + math.log2(math.e)
 
 
 def post_bits(cols: int) -> float:
-    """Bits of one post-grid entry under the gain criterion (F7)."""
+    """Bits of one post-grid entry under the gain criterion (FE7)."""
     return 16.0 + math.ceil(math.log2(cols))
 
 
 def _fit_pairs(v, E, nbits, lam, lo64, hi64, fallback):
-    """Codebooks by the best of the nine rule pairs (F2, F3), the per-group
-    choice by Eq. (5), and the fallback (F4)."""
+    """Codebooks by the best of the nine rule pairs (FE2, FE3), the per-group
+    choice by Eq. (5), and the fallback (FE4)."""
     lo0, s0 = initial_pair(lo64, hi64)
     pos = s0 > 0.0
     if pos.any():
@@ -292,7 +292,7 @@ def encode_full(w16: np.ndarray, group: int, nbits: int, E: Optional[np.ndarray]
     # 3. Base code of every entry from its original value (ties up).
     q = _base_code(wg, lo_f, s_f).astype(np.int64)
 
-    # 4. Post-grid guard, per output row (Appendix E "Guards", reading F7).
+    # 4. Post-grid guard, per output row (Appendix E "Guards", reading FE7).
     err2 = (Eg * (wg - (lo_f + s_f * q)) ** 2).reshape(R, C)
     free = ~mask.reshape(R, C)
     post = np.zeros((R, C), dtype=bool)
@@ -321,7 +321,7 @@ def encode_full(w16: np.ndarray, group: int, nbits: int, E: Optional[np.ndarray]
         planes[k - 3] = bk
         rec = rec + np.where(active, (2.0 * bk - 1.0) * s_f / 2.0 ** (k - 1), 0.0)
 
-    # 6. Side record, CSR by (row, col), the held-out weight itself (F8).
+    # 6. Side record, CSR by (row, col), the held-out weight itself (FE8).
     mask2 = mask.reshape(R, C)
     rr, cc = np.nonzero(mask2)
     row_ptr = np.zeros(R + 1, dtype=np.int64)

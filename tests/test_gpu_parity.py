@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import WORKLOADS, synth_matrix
+from workloads import WORKLOADS, synth_channel_energy, synth_matrix
 
 pytestmark = pytest.mark.gpu
 
@@ -407,3 +407,25 @@ def test_fp16_output_gemv(pwo, side, monkeypatch):
     assert pwo.lib().stagq_gemv_f16(m._h, xd.data_ptr(), None, yodd.data_ptr() + 1, 3, None) == -5
     assert pwo.lib().stagq_gemv_f16(m._h, xd.data_ptr(), None, yodd.data_ptr() + 2, 3, None) == 0
     torch.cuda.synchronize()
+
+
+@functools.lru_cache(maxsize=4)
+def _full_encoded(case, criterion):
+    R, Cc, g, N, dist, seed = case
+    w, x = synth_matrix(R, Cc, dist, seed)
+    return oracle.encode_full(w, g, N, E=synth_channel_energy(Cc, seed), criterion=criterion, tau=1e-4), x
+
+
+@pytest.mark.parametrize("criterion", ["ratio", "gain"])
+@pytest.mark.parametrize("side", ["0", "1"])
+def test_full_encoder_workload(pwo, criterion, side, monkeypatch):
+    """The oracle's full encoder as a second workload: codebooks placed by the
+    best of the nine rules, E_c-weighted pairs whose levels sit off the group
+    extremes, the ratio or gain criterion and per-row post-grid entries.  Codes
+    bit-exact and y to the parity bar in both side-record modes, on ragged rows,
+    g = 128 and 32, N = 4 and 6."""
+    monkeypatch.setenv("STAGQ_SIDE", side)
+    for case in ((72, 1024, 128, 4, "student_t", 21), (40, 512, 32, 6, "normal_outliers", 22)):
+        F, x = _full_encoded(case, criterion)
+        m, _ = _check(pwo, F, x, range(2, case[3] + 1), f"full encoder {criterion} {case} side={side}")
+        assert m.codebook

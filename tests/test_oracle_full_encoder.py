@@ -111,15 +111,15 @@ def test_uniform_weights_scale_out_of_the_choice():
     """Multiplying every E_c by the same power of two changes no choice (the
     loss scales exactly), and E_c = 1 gives the same fields as no E at all."""
     w, _ = synth_matrix(8, 128, "student_t", 6)
-    F1 = oracle.encode_full(w, 32, 4)
-    F2 = oracle.encode_full(w, 32, 4, E=np.full(128, 8.0))
-    F3 = oracle.encode_full(w, 32, 4, E=np.ones(128))
-    for F in (F2, F3):
-        assert np.array_equal(F.idx, F1.idx) and np.array_equal(F.q, F1.q)
-        assert np.array_equal(F.mask, F1.mask) and np.array_equal(F.planes, F1.planes)
+    Fa = oracle.encode_full(w, 32, 4)
+    Fb = oracle.encode_full(w, 32, 4, E=np.full(128, 8.0))
+    Fc = oracle.encode_full(w, 32, 4, E=np.ones(128))
+    for F in (Fb, Fc):
+        assert np.array_equal(F.idx, Fa.idx) and np.array_equal(F.q, Fa.q)
+        assert np.array_equal(F.mask, Fa.mask) and np.array_equal(F.planes, Fa.planes)
 
 
-# ------------------------------------------------------ rule choice (F3)
+# ------------------------------------------------------ rule choice (FE3)
 def _first_term_via_quantizer(vals, wts, lo, s, N):
     """First term of Eq. (5) through the single-value quantizer and the
     additive reconstruction of Eq. (9), one value at a time."""
@@ -237,7 +237,7 @@ def _d2_via_quantizer(vals, wts, lo, s):
 
 
 def test_gain_is_the_fall_in_two_bit_error_after_the_refit():
-    """Eq. (11) with reading F5, group by group: the pair re-picked by Eq. (5)
+    """Eq. (11) with reading FE5, group by group: the pair re-picked by Eq. (5)
     (checked in exact rationals) for the group as is and with its candidate
     clipped, and the two-bit errors recomputed through the single-value
     quantizer; the held-out set is exactly the gains per bit above tau."""
