@@ -81,6 +81,15 @@ typedef struct {
  *   codebook NULL: the image stores lo, s (4 bytes per group).  Otherwise the
  *            image stores the codebook metadata (1 byte per group, plus the 256
  *            pairs once), and lo, s must be the pairs the indices select.
+ *   side_slots  how the image stores the side record: 0 as CSR (row_ptr and
+ *            one entry per held-out weight; the GEMV reads row_ptr, then the
+ *            entries); W > 0 as W fixed slots per row ([StagQ] Appendix A and
+ *            Appendix E: the per-row slots the pages' kernel reads on the
+ *            feed-forward matrices), W at least the fullest row's count
+ *            (else STAGQ_ECSR) and at most 4096; -1 for W = the fullest row's
+ *            count (0 entries: CSR).  Fixed slots cost W * 8 bytes per row
+ *            whatever the row holds, and spare the GEMV the dependent row_ptr
+ *            read.
  * The planes must be 0 at held-out positions (section 3.6: the planes skip every
  * position the side record carries); q there is the base code of the original
  * weight.
@@ -96,6 +105,7 @@ typedef struct {
   const uint16_t* val;
   int64_t nnz;
   const stagq_codebook* codebook;
+  int32_t side_slots;
 } stagq_fields;
 
 /* Shape and traffic of a packed matrix. */
@@ -105,11 +115,12 @@ typedef struct {
   uint64_t image_bytes;      /* size of the packed image */
   /* Algorithmic bytes one GEMV at precision b moves, for b = 2..N (index b;
    * 0 elsewhere): base stream + planes 3..b + group metadata (4 bytes per group,
-   * or 1 byte per group plus the 1 KB table of 256 pairs) + row_ptr + side
-   * record (one 8-byte entry per held-out weight) + x (fp16) + y (fp32). */
+   * or 1 byte per group plus the 1 KB table of 256 pairs) + side record (CSR:
+   * row_ptr and one 8-byte entry per held-out weight; fixed slots: 8 bytes per
+   * slot of every row) + x (fp16) + y (fp32). */
   uint64_t bytes_read[9];
   int32_t codebook;          /* 1 if the image stores codebook metadata */
-  int32_t reserved;
+  int32_t side_slots;        /* fixed side-record slots per row; 0 for CSR */
 } stagq_info;
 
 /* Bytes of the packed image for these fields (0 if the shape is unsupported). */

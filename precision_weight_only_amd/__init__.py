@@ -80,18 +80,26 @@ def stream_read(buf, offset: int, nbytes: int, sink, stream=None) -> None:
                                   C.c_void_p(sink.data_ptr()), _stream_ptr(stream)), "stagq_stream_read")
 
 
-def packed_bytes(fields) -> int:
-    keep: list = []
-    return int(lib().stagq_packed_bytes(C.byref(fields_struct(fields, keep))))
+def _size_error(fs) -> None:
+    """stagq_packed_bytes gave 0: raise the status validation reports (the
+    packer validates before it looks at its destination)."""
+    st = int(lib().stagq_pack_host(C.byref(fs), None, 0))
+    check(st if st not in (0, -1) else -3, "stagq_packed_bytes")
 
 
-def pack_host(fields) -> np.ndarray:
-    """Packed image in host memory (uint8 array)."""
+def packed_bytes(fields, side_slots: int = 0) -> int:
     keep: list = []
-    fs = fields_struct(fields, keep)
+    return int(lib().stagq_packed_bytes(C.byref(fields_struct(fields, keep, side_slots))))
+
+
+def pack_host(fields, side_slots: int = 0) -> np.ndarray:
+    """Packed image in host memory (uint8 array).  side_slots: 0 CSR side
+    record, W > 0 fixed slots per row, -1 as many as the fullest row."""
+    keep: list = []
+    fs = fields_struct(fields, keep, side_slots)
     n = int(lib().stagq_packed_bytes(C.byref(fs)))
     if n == 0:
-        check(-3, "stagq_packed_bytes")
+        _size_error(fs)
     img = np.zeros(n, dtype=np.uint8)
     check(lib().stagq_pack_host(C.byref(fs), img.ctypes.data_as(C.c_void_p), n), "stagq_pack_host")
     return img
@@ -115,7 +123,8 @@ def unpack_host(image: np.ndarray) -> Dict:
     out["lo"] = out["lo"].view(np.float16)
     out["s"] = out["s"].view(np.float16)
     out["val"] = out["val"].view(np.float16)
-    out.update(rows=R, cols=Cc, group=g, nbits=N, nnz=nnz, codebook=int(info.codebook))
+    out.update(rows=R, cols=Cc, group=g, nbits=N, nnz=nnz, codebook=int(info.codebook),
+               side_slots=int(info.side_slots))
     return out
 
 
@@ -131,15 +140,18 @@ class StagQMatrix:
         self.image_bytes = info.image_bytes
         self.bytes_read = {b: int(info.bytes_read[b]) for b in range(2, self.nbits + 1)}
         self.codebook = bool(info.codebook)    # codebook metadata (else fp16 pairs)
+        self.side_slots = int(info.side_slots)  # fixed side-record slots per row (0: CSR)
 
     @classmethod
-    def pack(cls, fields, device="cuda:0", stream=None) -> "StagQMatrix":
+    def pack(cls, fields, device="cuda:0", stream=None, side_slots: int = 0) -> "StagQMatrix":
+        """side_slots: 0 CSR side record, W > 0 fixed slots per row, -1 as
+        many as the fullest row."""
         torch = _torch()
         keep: list = []
-        fs = fields_struct(fields, keep)
+        fs = fields_struct(fields, keep, side_slots)
         n = int(lib().stagq_packed_bytes(C.byref(fs)))
         if n == 0:
-            check(-3, "stagq_packed_bytes")
+            _size_error(fs)
         buf = torch.empty(n, dtype=torch.uint8, device=device)
         h = C.c_void_p()
         with torch.cuda.device(buf.device):

@@ -35,7 +35,7 @@ class Fields(C.Structure):
         ("rows", C.c_int32), ("cols", C.c_int32), ("group", C.c_int32), ("nbits_max", C.c_int32),
         ("q", C.c_void_p), ("planes", C.c_void_p), ("lo", C.c_void_p), ("s", C.c_void_p),
         ("row_ptr", C.c_void_p), ("col", C.c_void_p), ("val", C.c_void_p), ("nnz", C.c_int64),
-        ("codebook", C.c_void_p),
+        ("codebook", C.c_void_p), ("side_slots", C.c_int32),
     ]
 
 
@@ -43,7 +43,7 @@ class Info(C.Structure):
     _fields_ = [
         ("rows", C.c_int32), ("cols", C.c_int32), ("group", C.c_int32), ("nbits_max", C.c_int32),
         ("nnz", C.c_int64), ("image_bytes", C.c_uint64), ("bytes_read", C.c_uint64 * 9),
-        ("codebook", C.c_int32), ("reserved", C.c_int32),
+        ("codebook", C.c_int32), ("side_slots", C.c_int32),
     ]
 
 
@@ -107,10 +107,12 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(C.c_void_p) if a is not None and a.size else None
 
 
-def fields_struct(f, keep: list) -> Fields:
+def fields_struct(f, keep: list, side_slots: int = 0) -> Fields:
     """Marshal an unpacked field set (attributes or mapping: rows, cols, group,
     nbits, q, planes, lo, s, row_ptr, col, val) into the C struct.  Arrays are
-    converted to the C layout and appended to `keep` so they outlive the call."""
+    converted to the C layout and appended to `keep` so they outlive the call.
+    side_slots: 0 CSR side record, W > 0 fixed slots per row, -1 as many as the
+    fullest row."""
     get = (lambda k: f[k]) if isinstance(f, dict) else (lambda k: getattr(f, k))
     q = np.ascontiguousarray(get("q"), dtype=np.uint8)
     R, Cc = q.shape
@@ -133,4 +135,4 @@ def fields_struct(f, keep: list) -> Fields:
         keep.extend([idx, l2s, rat, cb])
     return Fields(R, Cc, group, nbits, _ptr(q), _ptr(planes), _ptr(lo), _ptr(s),
                   row_ptr.ctypes.data_as(C.c_void_p), _ptr(col), _ptr(val), int(col.shape[0]),
-                  C.cast(C.pointer(cb), C.c_void_p) if cb is not None else None)
+                  C.cast(C.pointer(cb), C.c_void_p) if cb is not None else None, int(side_slots))

@@ -146,6 +146,7 @@ struct GemvParams {
   uint32_t lds_flag;          // LDS offset of the per-wave x-staged flags (side-record wave mode)
   uint32_t lds_table;         // LDS offset of the per-wave copies of the 256 pairs (codebook metadata)
   int32_t flag_spins;         // spin limit of the side-record wave's wait for them
+  int32_t slots;              // fixed side-record slots per row (0: CSR)
 };
 
 template <int M, int GU>
@@ -399,6 +400,21 @@ constexpr int kXPitch = 68;      // LDS dwords per tile: 64 of x, then up to 4 g
 // the wait ends long before.
 constexpr int kFlagSpins = 1 << 20;
 
+// The side-record wave's wait for every main wave's "x staged" flag: true once
+// all are up, false if the spin limit ran out first (x_c then comes from global
+// memory, which gives bitwise the same values).
+__device__ __forceinline__ bool wait_x_staged(const GemvParams& p, int lane, const int32_t* flag_s) {
+  int spins = 0;
+  while (__builtin_amdgcn_ballot_w64(lane < p.S &&
+                                     __hip_atomic_load(flag_s + (lane < p.S ? lane : 0), __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_WORKGROUP) != 1) != 0) {
+    if (++spins > p.flag_spins) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  return spins <= p.flag_spins;
+}
+
 // Side-record wave (SIDE mode): the side record of one 16-row block, run by
 // the workgroup's extra wave while the others stream the main stream.
 // row_ptr -> entries are two dependent loads, and this wave issues no others,
@@ -431,17 +447,7 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
       const int e = cb + 64 * j + lane;
       ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
     }
-    if (cb == E0) {                      // wait once for every main wave's x
-      int spins = 0;
-      while (__builtin_amdgcn_ballot_w64(lane < p.S &&
-                                         __hip_atomic_load(flag_s + (lane < p.S ? lane : 0), __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_WORKGROUP) != 1) != 0) {
-        if (++spins > p.flag_spins) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      use_lds = spins <= p.flag_spins;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    }
+    if (cb == E0) use_lds = wait_x_staged(p, lane, flag_s);   // once, for every main wave's x
     const uint16_t* xh = reinterpret_cast<const uint16_t*>(xs);
     uint32_t xc[kSideBatches];
     if (use_lds) {
@@ -486,6 +492,64 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
   }
 }
 
+// Side-record wave with fixed slots (p.slots = W per row): lane = j0 * 16 +
+// row takes slots j0, j0 + 4, ... of its row; every address is known at once
+// (no row_ptr), so the wave's first loads go out with the main waves' first
+// steps.  Empty slots are zero entries (a = 0, s = 0) and add 0.  Each lane
+// sums its slots in order, then the four lanes of a row are added pairwise
+// (j0 0+1, 2+3, then the two sums): a fixed summation order.
+template <int M, bool SC>
+__device__ __forceinline__ void side_slots_wave(const GemvParams& p, int blk, int lane, float* rowc_s,
+                                                const int32_t* flag_s, const uint32_t* xs,
+                                                const rsrc_t& rSide, const rsrc_t& rX) {
+  constexpr float kHalfUlp = 2.0f / float(1 << M);   // 2^(1-M)
+  const int W = p.slots, j0 = lane >> 4;
+  const uint32_t e0 = uint32_t(blk) * uint32_t(W) * 16u + uint32_t(lane & 15);
+  const uint16_t* xh = reinterpret_cast<const uint16_t*>(xs);
+  float acc = 0.f;
+  bool use_lds = false;
+  for (int cb = 0; cb < W; cb += 4 * kSideBatches) {   // W >= 1: at least once
+    uint64_t ent[kSideBatches];
+#pragma unroll
+    for (int t = 0; t < kSideBatches; t++) {
+      const int j = cb + 4 * t + j0;
+      ent[t] = ld64side(rSide, j < W ? (e0 + uint32_t(j) * 16u) * 8u : kOOB);
+    }
+    if (cb == 0) {
+      __builtin_amdgcn_s_barrier();      // the main waves' flags are cleared
+      use_lds = wait_x_staged(p, lane, flag_s);
+    }
+    uint32_t xc[kSideBatches];
+    if (use_lds) {
+#pragma unroll
+      for (int t = 0; t < kSideBatches; t++) {
+        const int c = int(ent[t] >> 48);   // empty and out-of-range slots: column 0
+        xc[t] = xh[(c >> 7) * (2 * kXPitch) + (c & 127)];
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < kSideBatches; t++) xc[t] = ld16(rX, uint32_t(ent[t] >> 48) * 2u);
+      if constexpr (SC) {
+        const rsrc_t rS = mk(p.xsc, p.x_bytes);
+#pragma unroll
+        for (int t = 0; t < kSideBatches; t++)
+          xc[t] = hmul2(xc[t], ld16(rS, uint32_t(ent[t] >> 48) * 2u)) & 0xffffu;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kSideBatches; t++) {
+      if (cb + 4 * t >= W) break;        // no slots left (uniform)
+      const uint64_t ev = ent[t];
+      const float a = __builtin_bit_cast(float, uint32_t(ev));
+      const float st = h2f(uint32_t(ev >> 32) & 0xffffu);
+      acc += cb + 4 * t + j0 < W ? (a - st * kHalfUlp) * h2f(xc[t]) : 0.f;
+    }
+  }
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  if (lane < 16) rowc_s[lane] = acc;
+}
+
 // The GEMV.  SIDE selects where the side record is applied: by an extra wave
 // of the workgroup (SIDE = 1, for grids with several workgroups per CU, where
 // its latency hides behind other workgroups) or by all waves after the main
@@ -513,7 +577,10 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
 
   if constexpr (SIDE) {
     if (w == p.S) {                      // the side-record wave
-      side_record<M, SC>(p, blk, lane, rp_s, runs_s, flag_s, xs, rRp, rSide, rX);
+      if (p.slots)
+        side_slots_wave<M, SC>(p, blk, lane, runs_s, flag_s, xs, rSide, rX);
+      else
+        side_record<M, SC>(p, blk, lane, rp_s, runs_s, flag_s, xs, rRp, rSide, rX);
       __syncthreads();
       return;
     }
@@ -533,8 +600,9 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   //     the x of this wave's tile columns, step 0 of the weights; steps
   //     1..D-1 follow once the x is staged.
   uint32_t rpv = 0;
-  if constexpr (!SIDE)
-    rpv = ld32(rRp, lane <= 16 ? uint32_t(min(blk * 16 + lane, p.R)) * 4u : kOOB);
+  if constexpr (!SIDE) {
+    if (!p.slots) rpv = ld32(rRp, lane <= 16 ? uint32_t(min(blk * 16 + lane, p.R)) * 4u : kOOB);
+  }
   const int cbase = 4 * q0 * 16;                         // first x chunk (8 columns) of the wave
   // x chunks of the wave's quads (those past the row's end, in its zero
   // tiles, load as zeros)
@@ -572,13 +640,24 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   const int tid = threadIdx.x, nthr = 64 * p.S;
   int E0 = 0, E1 = 0;
   uint64_t ent[kEntries];
+  // (fixed slots: thread tid takes slots tid / 16 + j * threads / 16 of row
+  // tid mod 16; no row_ptr)
+  const uint32_t se0 = uint32_t(blk) * uint32_t(p.slots) * 16u + uint32_t(tid & 15);
   if constexpr (!SIDE) {
-    E0 = __builtin_amdgcn_readlane(int(rpv), 0);
-    E1 = __builtin_amdgcn_readlane(int(rpv), 16);
+    if (p.slots) {
 #pragma unroll
-    for (int j = 0; j < kEntries; j++) {
-      const int e = E0 + j * nthr + tid;
-      ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
+      for (int j = 0; j < kEntries; j++) {
+        const int sj = (tid >> 4) + j * (nthr >> 4);
+        ent[j] = ld64side(rSide, sj < p.slots ? (se0 + uint32_t(sj) * 16u) * 8u : kOOB);
+      }
+    } else {
+      E0 = __builtin_amdgcn_readlane(int(rpv), 0);
+      E1 = __builtin_amdgcn_readlane(int(rpv), 16);
+#pragma unroll
+      for (int j = 0; j < kEntries; j++) {
+        const int e = E0 + j * nthr + tid;
+        ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
+      }
     }
   }
 
@@ -679,6 +758,37 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   //     order.
   constexpr float kHalfUlp = 2.0f / float(1 << M);   // 2^(1-M)
   const uint16_t* xh = reinterpret_cast<const uint16_t*>(xs);
+  if (p.slots) {
+    // --- ... or (fixed slots) each thread's slots in order, then the row's
+    //     owner adds the 4 S slot groups of its row in order.
+    const int W = p.slots, sstep = nthr >> 4;
+    float v = 0.f;
+    for (int cb = 0; cb < W; cb += kEntries * sstep) {
+      if (cb > 0) {                      // rare: more slots than one prefetched chunk
+#pragma unroll
+        for (int j = 0; j < kEntries; j++) {
+          const int sj = cb + (tid >> 4) + j * sstep;
+          ent[j] = ld64side(rSide, sj < W ? (se0 + uint32_t(sj) * 16u) * 8u : kOOB);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kEntries; j++) {
+        const int sj = cb + (tid >> 4) + j * sstep;
+        const uint64_t ev = ent[j];
+        const float a = __builtin_bit_cast(float, uint32_t(ev));
+        const float st = h2f(uint32_t(ev >> 32) & 0xffffu);
+        const int c = int(ev >> 48);
+        if (sj < W) v += (a - st * kHalfUlp) * h2f(xh[(c >> 7) * (2 * kXPitch) + (c & 127)]);
+      }
+    }
+    runs_s[(tid >> 4) * 17 + (tid & 15)] = v;
+    __syncthreads();
+    if (owner) {
+      for (int k = 0; k < sstep; k++) acc += runs_s[k * 17 + lane];
+      if (row_ok) store_y(p.y, p.y16, r, acc);
+    }
+    return;
+  }
   const int echunk = kEntries * nthr;
   for (int cb = E0; cb < E1; cb += echunk) {
     if (cb > E0) {                       // rare: more entries than one prefetched chunk
@@ -842,7 +952,7 @@ static size_t lds_layout(int C, int S, bool cb, dev::GemvParams* prm) {
   o += 18 * 4;
   o = (o + 15) & ~size_t(15);
   if (prm) prm->lds_runs = uint32_t(o);
-  o += size_t(dev::kEntries) * S * 17 * 4;
+  o += size_t(std::max(dev::kEntries, 4)) * S * 17 * 4;   // CSR run sums, or 4 S slot groups
   if (prm) prm->lds_flag = uint32_t(o);
   o += size_t(kMaxWaves) * 4;
   o = (o + 15) & ~size_t(15);
@@ -979,6 +1089,7 @@ int stagq_query(stagq_handle h, stagq_info* out) {
   out->rows = h->hdr.rows; out->cols = h->hdr.cols; out->group = h->hdr.group;
   out->nbits_max = h->hdr.nbits; out->nnz = h->hdr.nnz; out->image_bytes = h->hdr.total;
   out->codebook = h->hdr.codebook;
+  out->side_slots = h->hdr.side_slots;
   for (int b = 2; b <= h->hdr.nbits; b++) out->bytes_read[b] = bytes_read(h->hdr, b);
   return STAGQ_OK;
 }
@@ -1010,7 +1121,9 @@ static int gemv_call(stagq_handle h, const void* x, const void* x_scale, bool sc
   c.prm.y16 = half ? static_cast<uint16_t*>(y) : nullptr;
   c.prm.unit_bytes = uint32_t(H.unit_bytes);
   c.prm.units_bytes = uint32_t(uint64_t(H.blocks) * H.quads * H.unit_bytes);
-  c.prm.side_bytes = uint32_t(H.nnz * 8);
+  c.prm.side_bytes = uint32_t(H.side_slots ? uint64_t(H.rows_padded) * uint64_t(H.side_slots) * 8
+                                            : uint64_t(H.nnz) * 8);
+  c.prm.slots = H.side_slots;
   c.prm.rp_bytes = uint32_t((int64_t(H.rows) + 1) * 4);
   c.prm.x_bytes = uint32_t(H.cols * 2);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);

@@ -64,6 +64,19 @@ void codebook_pairs(const stagq_codebook* cb, uint32_t* out) {
   }
 }
 
+// Fixed side-record slots per row the image uses for f (reading f->row_ptr
+// only for -1, "as many as the fullest row"); -1 when the request is below the
+// fullest row or out of range.
+static int32_t resolve_slots(const stagq_fields* f) {
+  if (f->side_slots == 0) return 0;
+  if (f->side_slots < -1 || f->side_slots > kMaxSlots) return -1;
+  if (!f->row_ptr) return -1;
+  int64_t most = 0;
+  for (int64_t r = 0; r < f->rows; r++) most = std::max<int64_t>(most, int64_t(f->row_ptr[r + 1]) - f->row_ptr[r]);
+  if (f->side_slots == -1) return most <= kMaxSlots ? int32_t(most) : -1;
+  return f->side_slots >= most ? f->side_slots : -1;
+}
+
 int validate_fields(const stagq_fields* f, ImageHeader* h) {
   if (!f) return STAGQ_EINVAL;
   const stagq_codebook* cb = f->codebook;
@@ -101,18 +114,23 @@ int validate_fields(const stagq_fields* f, ImageHeader* h) {
         if (f->planes[k * n + r * C + c]) return STAGQ_EFIELD;  // planes skip held-out entries
     }
   }
+  const int32_t W = resolve_slots(f);
+  if (W < 0) return STAGQ_ECSR;
+  if (!layout(f->rows, f->cols, f->group, f->nbits_max, f->nnz, h, cb != nullptr, W)) return STAGQ_ESHAPE;
   return STAGQ_OK;
 }
 
-// Bytes one GEMV moves: base stream, planes 3..bits, group pairs, the side
-// record (row_ptr and 8 B per entry), x and y.  Padding rows of the last
-// 64-row block are not counted.
+// Bytes one GEMV moves: base stream, planes 3..bits, group metadata, the side
+// record (CSR: row_ptr and 8 B per entry; fixed slots: 8 B per slot of every
+// row, the pages' per-row slot accounting), x and y.  Padding rows of the last
+// 16-row block are not counted.
 uint64_t bytes_read(const ImageHeader& h, int bits) {
   const uint64_t n = uint64_t(h.rows) * h.cols;
   const uint64_t meta = h.codebook ? uint64_t(h.rows) * (h.cols / h.group) + 1024
                                    : uint64_t(h.rows) * (h.cols / h.group) * 4;
-  return n * 2 / 8 + n * uint64_t(bits - 2) / 8 + meta + uint64_t(h.rows + 1) * 4 + uint64_t(h.nnz) * 8 +
-         uint64_t(h.cols) * 2 + uint64_t(h.rows) * 4;
+  const uint64_t side = h.side_slots ? uint64_t(h.rows) * uint64_t(h.side_slots) * 8
+                                     : uint64_t(h.rows + 1) * 4 + uint64_t(h.nnz) * 8;
+  return n * 2 / 8 + n * uint64_t(bits - 2) / 8 + meta + side + uint64_t(h.cols) * 2 + uint64_t(h.rows) * 4;
 }
 
 // ----------------------------------------------------------------- pack ----
@@ -187,8 +205,10 @@ const char* stagq_strerror(int status) {
 
 size_t stagq_packed_bytes(const stagq_fields* f) {
   if (!f) return 0;
+  const int32_t W = resolve_slots(f);
+  if (W < 0) return 0;
   ImageHeader h;
-  if (!layout(f->rows, f->cols, f->group, f->nbits_max, f->nnz, &h, f->codebook != nullptr)) return 0;
+  if (!layout(f->rows, f->cols, f->group, f->nbits_max, f->nnz, &h, f->codebook != nullptr, W)) return 0;
   return size_t(h.total);
 }
 
@@ -219,7 +239,8 @@ int stagq_pack_host(const stagq_fields* f, void* dst, size_t dst_bytes) {
       const float af = float(a);
       uint32_t abits;
       memcpy(&abits, &af, 4);
-      side[e] = uint64_t(abits) | (uint64_t(f->s[gidx]) << 32) | (uint64_t(c) << 48);
+      const uint64_t at = h.side_slots ? slot_entry(r, e - f->row_ptr[r], h.side_slots) : uint64_t(e);
+      side[at] = uint64_t(abits) | (uint64_t(f->s[gidx]) << 32) | (uint64_t(c) << 48);
       sval[e] = f->val[e];
     }
   return STAGQ_OK;
@@ -234,12 +255,14 @@ int stagq_unpack_host(const void* image, size_t image_bytes, stagq_info* shape, 
   memcpy(&h, image, sizeof(h));
   if (h.magic != kImageMagic || h.version != kImageVersion) return STAGQ_EIMAGE;
   ImageHeader chk;
-  if (!layout(h.rows, h.cols, h.group, h.nbits, h.nnz, &chk, h.codebook != 0) || chk.total != h.total)
+  if (!layout(h.rows, h.cols, h.group, h.nbits, h.nnz, &chk, h.codebook != 0, h.side_slots) ||
+      chk.total != h.total)
     return STAGQ_EIMAGE;
   if (image_bytes < h.total) return STAGQ_ESIZE;
   memset(shape, 0, sizeof(*shape));
   shape->rows = h.rows; shape->cols = h.cols; shape->group = h.group; shape->nbits_max = h.nbits;
   shape->nnz = h.nnz; shape->image_bytes = h.total; shape->codebook = h.codebook;
+  shape->side_slots = h.side_slots;
   for (int b = 2; b <= h.nbits; b++) shape->bytes_read[b] = bytes_read(h, b);
   const uint8_t* img = static_cast<const uint8_t*>(image);
   const int64_t R = h.rows, C = h.cols, T = C / kTileCols, n = R * C;
@@ -265,13 +288,19 @@ int stagq_unpack_host(const void* image, size_t image_bytes, stagq_info* shape, 
         if (s) s[r * G + t * GU + gi] = uint16_t(mw >> 16);
       }
     }
-  if (row_ptr) memcpy(row_ptr, img + h.off_rowptr, size_t(R + 1) * 4);
+  const int32_t* rp = reinterpret_cast<const int32_t*>(img + h.off_rowptr);
+  if (rp[0] != 0 || rp[R] != h.nnz) return STAGQ_EIMAGE;
+  for (int64_t r = 0; r < R; r++)
+    if (rp[r + 1] < rp[r] || (h.side_slots && rp[r + 1] - rp[r] > h.side_slots)) return STAGQ_EIMAGE;
+  if (row_ptr) memcpy(row_ptr, rp, size_t(R + 1) * 4);
   const uint64_t* side = reinterpret_cast<const uint64_t*>(img + h.off_side);
   const uint16_t* sval = reinterpret_cast<const uint16_t*>(img + h.off_sideval);
-  for (int64_t e = 0; e < h.nnz; e++) {
-    if (col) col[e] = int32_t(side[e] >> 48);
-    if (val) val[e] = sval[e];
-  }
+  for (int64_t r = 0; r < R; r++)
+    for (int64_t e = rp[r]; e < rp[r + 1]; e++) {
+      const uint64_t at = h.side_slots ? slot_entry(r, e - rp[r], h.side_slots) : uint64_t(e);
+      if (col) col[e] = int32_t(side[at] >> 48);
+      if (val) val[e] = sval[e];
+    }
   return STAGQ_OK;
 }
 

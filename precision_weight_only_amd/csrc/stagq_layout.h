@@ -30,6 +30,11 @@
 //                    bits  0..31  a = P - lo - s (q - 1/2) as fp32
 //                    bits 32..47  the group step s (fp16)
 //                    bits 48..63  the column
+//                  or, with fixed slots (side_slots = W > 0), W slots per row
+//                  in order of block, slot, row of the block: entry k of row r
+//                  (in column order) at ((r / 16) W + k) 16 + r mod 16, empty
+//                  slots all zero (a = 0, s = 0: a correction of 0).  The GEMV
+//                  then reads the slots of a block without row_ptr.
 //   side values    the recorded weights P (fp16), for unpacking only
 //
 // Bit placement inside a tile (column c = 0..127 of the tile):
@@ -50,7 +55,8 @@ constexpr int kTileCols = 128;
 constexpr int kBlockRows = 16;
 constexpr int kMaxCols = 32768;   // x is staged whole in LDS (64 KB)
 constexpr uint32_t kImageMagic = 0x51474153u;  // "SAGQ"
-constexpr uint32_t kImageVersion = 5;
+constexpr uint32_t kImageVersion = 6;
+constexpr int kMaxSlots = 4096;        // fixed side-record slots per row, at most
 constexpr int kUnitTiles = 64;         // tiles per unit: 16 rows x 4 tile columns
 constexpr int kChunkStride = 1024;     // bytes of one 16-byte chunk over a unit's 64 tiles
 constexpr int kMaxBits = 8;
@@ -65,7 +71,8 @@ struct ImageHeader {           // first 256 bytes of an image
   uint64_t off_units, unit_bytes, unit_meta_bytes;  // unit array; bytes per unit; metadata per unit
   uint64_t off_rowptr, off_side, off_sideval, total;
   uint64_t off_table;          // codebook metadata: the 256 pairs (0 otherwise)
-  uint64_t pad[17];
+  int32_t side_slots, spare;   // W > 0: fixed side-record slots per row; 0: CSR
+  uint64_t pad[16];
 };
 static_assert(sizeof(ImageHeader) == 256, "image header is 256 bytes");
 
@@ -99,15 +106,21 @@ inline uint64_t unit_plane_dword(const ImageHeader& h, int k, int t, int d) {
   return h.unit_meta_bytes + uint64_t(k - 1) * kChunkStride + uint64_t(t) * 16 + uint64_t(d) * 4;
 }
 
+// Entry index of slot k of row r in a fixed-slot side record of W slots per row.
+inline uint64_t slot_entry(int64_t r, int64_t k, int32_t W) {
+  return (uint64_t(r / kBlockRows) * uint64_t(W) + uint64_t(k)) * kBlockRows + uint64_t(r % kBlockRows);
+}
+
 // Fill in every size and offset of an image; returns false for an unsupported
 // shape (the caller maps that to STAGQ_ESHAPE).
 inline bool layout(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int64_t nnz,
-                   ImageHeader* h, bool codebook = false) {
+                   ImageHeader* h, bool codebook = false, int32_t side_slots = 0) {
   if (rows < 0 || rows > (1 << 30) || cols <= 0 || cols % kTileCols != 0 || cols > kMaxCols)
     return false;
   if (group != 32 && group != 64 && group != 128) return false;
   if (nbits < 2 || nbits > kMaxBits) return false;
   if (nnz < 0 || nnz >= (int64_t(1) << 28)) return false;  // side record below 2 GiB
+  if (side_slots < 0 || side_slots > kMaxSlots) return false;
   *h = ImageHeader{};
   h->magic = kImageMagic;
   h->version = kImageVersion;
@@ -117,6 +130,7 @@ inline bool layout(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int
   h->tiles = int64_t(h->rows_padded) * padded_tcols(cols);
   h->quads = int32_t(padded_tcols(cols) / 4);
   h->codebook = codebook ? 1 : 0;
+  h->side_slots = side_slots;
   h->unit_meta_bytes = uint64_t(kUnitTiles) * (kTileCols / group) * (codebook ? 1 : 4);
   h->unit_bytes = h->unit_meta_bytes + uint64_t(nbits) * kChunkStride;
   const uint64_t units = uint64_t(h->blocks) * h->quads;
@@ -126,7 +140,10 @@ inline bool layout(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int
   if (codebook) { h->off_table = o; o += 1024; }
   h->off_units = o;   o = align256(o + units * h->unit_bytes);
   h->off_rowptr = o;  o = align256(o + uint64_t(rows + 1) * 4);
-  h->off_side = o;    o = align256(o + uint64_t(nnz) * 8);
+  // side entries: one per held-out weight, or W slots per (padded) row
+  const uint64_t side_entries = side_slots ? uint64_t(h->rows_padded) * uint64_t(side_slots) : uint64_t(nnz);
+  if (side_entries * 8 >= (uint64_t(1) << 31)) return false;
+  h->off_side = o;    o = align256(o + side_entries * 8);
   h->off_sideval = o; o = align256(o + uint64_t(nnz) * 2);
   h->total = o;
   return true;

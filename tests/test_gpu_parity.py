@@ -66,8 +66,8 @@ def _encoded(workload, mname):
     return F, x
 
 
-def _check(pwo, F, x, bits, tag, codes_rows=None):
-    m = pwo.StagQMatrix.pack(F)
+def _check(pwo, F, x, bits, tag, codes_rows=None, side_slots=0):
+    m = pwo.StagQMatrix.pack(F, side_slots=side_slots)
     xd = _to_dev(x)
     for M in bits:
         _say(tag, f"bits={M}", f"shape={F.rows}x{F.cols}", f"g={F.group}", f"nnz={F.nnz}")
@@ -429,3 +429,46 @@ def test_full_encoder_workload(pwo, criterion, side, monkeypatch):
         F, x = _full_encoded(case, criterion)
         m, _ = _check(pwo, F, x, range(2, case[3] + 1), f"full encoder {criterion} {case} side={side}")
         assert m.codebook
+        # the pages' pairing: per-row post-grid picks in fixed per-row slots
+        m, _ = _check(pwo, F, x, (2, case[3]), f"full encoder {criterion} {case} side={side} slots",
+                      side_slots=-1)
+        assert m.side_slots == int(np.diff(F.row_ptr).max())
+
+
+@pytest.mark.parametrize("side", ["0", "1"])
+def test_fixed_slot_side_record(pwo, side, monkeypatch):
+    """The side record in fixed per-row slots (no row_ptr on the GEMV's path):
+    codes bit-exact and y to the parity bar against the oracle in both
+    side-record modes, with W the fullest row's count and with spare slots, on
+    ragged rows and on rows of several hundred entries (many slot batches);
+    the side-record wave's global-x fallback gives bitwise the same y; with the
+    AWQ scale and with an fp16 result too."""
+    import torch
+    monkeypatch.setenv("STAGQ_SIDE", side)
+    rng = np.random.default_rng(43)
+    for case in ((256, 512, 64, 4, 0.005, "normal_outliers", 0), (1001, 384, 64, 4, 0.01, "student_t", 2),
+                 (64, 4096, 128, 4, 0.1, "normal_outliers", 5), (77, 640, 32, 6, 0.02, "student_t", 3)):
+        R, Cc, g, N, frac, dist, seed = case
+        w, x = synth_matrix(R, Cc, dist, seed)
+        F = oracle.encode(w, g, N, frac)
+        W = int(np.diff(F.row_ptr).max())
+        for slots in (-1, W + 5):
+            tag = f"slots={slots} (fullest row {W}) {case} side={side}"
+            m, xd = _check(pwo, F, x, range(2, N + 1), tag, side_slots=slots)
+            assert m.side_slots == (W if slots == -1 else slots)
+        a = rng.uniform(0.5, 2.0, Cc).astype(np.float16)
+        ad = _to_dev(a)
+        for M in (2, N):
+            _say(f"slots {case} side={side} awq / fp16 out / fallback", f"bits={M}")
+            y = m.gemv(xd, M, x_scale=ad).cpu().numpy()
+            ref = oracle.gemv_scaled(F, x, a, M)
+            assert _rel(y, ref) <= REL_L2_CONTRACT
+            assert _regression_ok(y, ref, F, oracle.scale_x(x, a), M)
+            y32 = m.gemv(xd, M).cpu().numpy()
+            y16 = m.gemv(xd, M, out_dtype=torch.float16).cpu().numpy()
+            assert np.array_equal(y16.view(np.uint16), y32.astype(np.float16).view(np.uint16))
+            if side == "1":
+                monkeypatch.setenv("STAGQ_FLAG_SPINS", "0")
+                assert np.array_equal(m.gemv(xd, M).cpu().numpy(), y32)
+                assert np.array_equal(m.gemv(xd, M, x_scale=ad).cpu().numpy(), y)
+                monkeypatch.delenv("STAGQ_FLAG_SPINS")

@@ -229,3 +229,59 @@ def test_codebook_metadata_validation():
     with pytest.raises(pwo.StagQError) as e:
         pwo.pack_host(bad)
     assert e.value.status == -1
+
+
+def test_fixed_slot_side_record_layout_and_bytes():
+    """Fixed side-record slots (the pages' per-row slots): with W = the fullest
+    row's count the image round-trips to the same CSR; entry k of row r sits at
+    entry ((r / 16) W + k) 16 + r mod 16 of the side region with its column in
+    bits 48..63, every other slot is zero; the GEMV's byte count charges W * 8
+    bytes per row and no row_ptr."""
+    w, _ = synth_matrix(40, 384, "normal_outliers", 18)     # 40 rows: a ragged last block
+    F = oracle.encode(w, 64, 4, 0.01)
+    counts = np.diff(F.row_ptr)
+    W = int(counts.max())
+    assert W >= 2 and counts.min() < W
+    img = pwo.pack_host(F, side_slots=-1)
+    assert img.size == pwo.packed_bytes(F, side_slots=-1)
+    U = pwo.unpack_host(img)
+    assert U["side_slots"] == W
+    for k in ("q", "planes", "row_ptr", "col"):
+        assert np.array_equal(getattr(F, k), U[k]), k
+    for k in ("lo", "s", "val"):
+        assert np.array_equal(getattr(F, k).view(np.uint16), U[k].view(np.uint16)), k
+    hdr = img[:256].view(np.uint64)
+    off_side = int(hdr[11])
+    slots = img[off_side:off_side + 48 * W * 8].view(np.uint64)   # 3 blocks of 16 rows
+    seen = np.zeros(slots.size, bool)
+    for r in range(F.rows):
+        for k, e in enumerate(range(F.row_ptr[r], F.row_ptr[r + 1])):
+            at = ((r // 16) * W + k) * 16 + r % 16
+            assert int(slots[at]) >> 48 == F.col[e]
+            seen[at] = True
+    assert not slots[~seen].any()
+    Wx = W + 3
+    img2 = pwo.pack_host(F, side_slots=Wx)
+    info, info0 = _lib.Info(), _lib.Info()
+    for im, inf in ((img2, info), (pwo.pack_host(F), info0)):
+        pwo.lib().stagq_unpack_host(im.ctypes.data_as(C.c_void_p), im.size, C.byref(inf),
+                                    None, None, None, None, None, None, None)
+    assert info.side_slots == Wx and info0.side_slots == 0
+    for M in (2, 3, 4):
+        assert info.bytes_read[M] - 40 * Wx * 8 == info0.bytes_read[M] - 41 * 4 - F.nnz * 8
+
+
+def test_fixed_slot_side_record_validation():
+    """Fewer slots than the fullest row, more than 4096, or a negative count
+    other than -1 are STAGQ_ECSR; -1 with an empty side record keeps CSR."""
+    w, _ = synth_matrix(16, 256, "student_t", 19)
+    F = oracle.encode(w, 128, 4, 0.02)
+    W = int(np.diff(F.row_ptr).max())
+    for bad in (W - 1, 4097, -2):
+        with pytest.raises(pwo.StagQError) as e:
+            pwo.pack_host(F, side_slots=bad)
+        assert e.value.status == -4, bad
+        assert pwo.packed_bytes(F, side_slots=bad) == 0
+    F0 = oracle.encode(w, 128, 4, 0.0)
+    assert pwo.unpack_host(pwo.pack_host(F0, side_slots=-1))["side_slots"] == 0
+    assert pwo.unpack_host(pwo.pack_host(F, side_slots=4096))["side_slots"] == 4096
