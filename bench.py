@@ -172,14 +172,15 @@ def sweep(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     rows = []
-    for wname in ("attn", "mlp", "phi4_mlp", "layer_sweep"):
+    for wname in ("attn", "mlp", "mlp_rows", "phi4_mlp", "layer_sweep"):
         wl = WORKLOADS[wname]
         for mat in wl.matrices:
             w, x = synth_matrix(mat.rows, mat.cols, wl.dist, mat.seed)
             K = int(np.floor(wl.frac * mat.rows * mat.cols + 0.5))
-            fields = pwo.encode(w, wl.group, wl.nbits, K, wl.ratio_T)
+            fields = pwo.encode(w, wl.group, wl.nbits, K, wl.ratio_T, post_per_row=wl.post_per_row)
             del w
             base = pwo.StagQMatrix.pack(fields, device=dev)
+            slm = pwo.StagQMatrix.pack(fields, device=dev, side_slots=-1) if wl.post_per_row else None
             cbm = pwo.StagQMatrix.pack(codebook_fields(fields), device=dev) if wname == "mlp" else None
             del fields
             n_copies = max(2, -(-args.rot_mb * (1 << 20) // base.bytes_read[min(wl.bits)]))
@@ -233,6 +234,20 @@ def sweep(args):
                     entry["bits"][str(M)]["codebook"] = {"us": round(us, 3), "bytes": int(b),
                                                          "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2)}
                 del cbc, cbm
+            if slm is not None:
+                # the same fields with the side record in fixed per-row slots
+                slc = [slm] + [slm.replicate() for _ in range(n_copies - 1)]
+
+                def launch_sl(c, M):
+                    slc[c].gemv(xd, M, y=ys[c])
+
+                for M in wl.bits:
+                    us = graph_time(launch_sl, n_copies, args.steps, [M])
+                    b = slm.bytes_read[M]
+                    entry["bits"][str(M)]["slots"] = {"us": round(us, 3), "bytes": int(b), "W": slm.side_slots,
+                                                      "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2)}
+                del slc
+            del slm
             if wname == "layer_sweep":
                 us = graph_time(launch, n_copies, args.steps, list(wl.bits))
                 b = sum(base.bytes_read[M] for M in wl.bits) / len(wl.bits)
@@ -242,7 +257,8 @@ def sweep(args):
                   " ".join(f"{M}b {v['us']}us {v['pct_peak']}%" +
                            (f" (awq {v['awq_scaled_us']}us)" if "awq_scaled_us" in v else "") +
                            (f" (fp16 out {v['fp16_out_us']}us)" if "fp16_out_us" in v else "") +
-                           (f" (codebook {v['codebook']['us']}us)" if "codebook" in v else "")
+                           (f" (codebook {v['codebook']['us']}us)" if "codebook" in v else "") +
+                           (f" (slots W={v['slots']['W']} {v['slots']['us']}us)" if "slots" in v else "")
                            for M, v in entry["bits"].items()),
                   file=sys.stderr, flush=True)
             del copies, base, ys

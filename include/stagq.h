@@ -246,18 +246,26 @@ const char* stagq_strerror(int status);
  * pre-grid guard (at most one entry per group whose magnitude exceeds ratio_T
  * times the group's second largest, ranked by that ratio), min-max pair fit over
  * the remaining entries stored as fp16, nearest base code (ties upward),
- * post-grid guard on the largest two-bit residuals of the matrix, and planes
- * that store the sign of the residual of the preceding prefix (sign(0) = +1),
- * skipping held-out positions.  budget is the side-record size K.
+ * post-grid guard, and planes that store the sign of the residual of the
+ * preceding prefix (sign(0) = +1), skipping held-out positions.
+ *   budget        side-record size K (post_per_row = 0), or the cap of the
+ *                 pre-grid guard alone (post_per_row > 0)
+ *   post_per_row  0: the post-grid guard fills the budget with the largest
+ *                 two-bit residuals |w - (lo + s q)| of the matrix (ties by
+ *                 flat index); k > 0: it takes the k largest of every row (ties
+ *                 by column; [StagQ] Appendix E picks per output row, there
+ *                 activation-weighted; here every channel weighs the same)
  *   w       host fp16 [rows*cols]
  *   outputs host, caller-allocated: q [rows*cols], planes [(N-2)*rows*cols],
- *           lo, s [rows*cols/group], row_ptr [rows+1], col [budget], val [budget];
+ *           lo, s [rows*cols/group], row_ptr [rows+1], col and val
+ *           [budget + rows*post_per_row] (row_ptr[rows] entries are written);
  *           *n_pre receives how many entries the pre-grid guard took.
  * group may be any divisor of cols here (packing restricts it further).
  */
 int stagq_encode(const uint16_t* w, int32_t rows, int32_t cols, int32_t group, int32_t nbits,
-                 int64_t budget, double ratio_T, uint8_t* q, uint8_t* planes, uint16_t* lo,
-                 uint16_t* s, int32_t* row_ptr, int32_t* col, uint16_t* val, int64_t* n_pre);
+                 int64_t budget, double ratio_T, int32_t post_per_row, uint8_t* q, uint8_t* planes,
+                 uint16_t* lo, uint16_t* s, int32_t* row_ptr, int32_t* col, uint16_t* val,
+                 int64_t* n_pre);
 
 /*
  * Inverse of stagq_pack_host for a host copy of an image (layout round-trip

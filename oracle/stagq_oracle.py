@@ -44,7 +44,10 @@ R3  Pre-grid guard = ratio criterion with T = 4 (section 3.5, Table 6): in
 R4  Post-grid guard: the remaining budget K - K_pre goes to the entries with
     the largest two-bit residual |w - (lo + s q)| over the whole matrix (ties
     by flat index).  The paper picks per output row with activation weights
-    (Appendix E); without calibration data a global unweighted pick is used.
+    (Appendix E); encode(..., post_per_row=k) takes the k largest residuals of
+    every row instead (ties by column, every channel weighing the same; K then
+    caps the pre-grid guard only).  The full encoder in stagq_encoder_full.py
+    has the activation-weighted per-row pick.
 R5  Held-out entries keep the base code of their original value and all-zero
     planes: the planes "skip every position the side record already carries"
     (section 3.6), and Eq. (4)'s (1 - m) removes whatever the main stream
@@ -227,13 +230,15 @@ def pair_loss(v, lo, s, nbits: int, lam: float = 4.0, E=None):
 
 
 def encode(w16: np.ndarray, group: int, nbits: int, frac: float, T: float = 4.0,
-           pair_fit: str = "minmax", lam: float = 4.0) -> Fields:
+           pair_fit: str = "minmax", lam: float = 4.0, post_per_row: int = 0) -> Fields:
     """The reference encoder.  pair_fit "minmax": the pair of R2, stored as two
     fp16 numbers per group.  pair_fit "codebook": the pages' metadata (section
     3.1): codebooks fitted to the initial pairs of Appendix B by uniform
     placement, then per group the index whose (lo, s) minimizes Eq. (5) (E_c = 1,
     lambda = lam) over the group with its pre-grid entry clipped to the next
-    value inward (R11); every later step uses the chosen pair."""
+    value inward (R11); every later step uses the chosen pair.  post_per_row
+    = k > 0: the post-grid guard takes the k largest two-bit residuals of every
+    row, and the budget caps the pre-grid guard only (R4)."""
     if pair_fit not in ("minmax", "codebook"):
         raise ValueError("pair_fit must be 'minmax' or 'codebook'")
     w16 = np.asarray(w16)
@@ -302,10 +307,19 @@ def encode(w16: np.ndarray, group: int, nbits: int, frac: float, T: float = 4.0,
         q += (d >= (j + 0.5) * s_f)
     q = np.where(s_f > 0.0, q, 0)
 
-    # 4. Post-grid guard: largest two-bit residuals over the matrix (R4).
+    # 4. Post-grid guard: largest two-bit residuals over the matrix, or the
+    #    post_per_row largest of every row (R4).
     r2 = np.abs(wg - (lo_f + s_f * q))
-    n_post = K - n_pre
-    if n_post > 0:
+    n_post = 0 if post_per_row else K - n_pre
+    if post_per_row > 0:
+        m2 = mask.reshape(R, C)                     # a view: writes go to mask
+        r2r = r2.reshape(R, C)
+        for r in range(R):
+            free_cols = np.nonzero(~m2[r])[0]
+            order = np.lexsort((free_cols, -r2r[r, free_cols]))[:post_per_row]
+            m2[r, free_cols[order]] = True
+            n_post += int(order.shape[0])
+    if n_post > 0 and not post_per_row:
         free_flat = flat[~mask]                     # ascending flat index
         free_r2 = r2[~mask]
         if n_post >= free_r2.shape[0]:

@@ -39,23 +39,29 @@ def _stream_ptr(stream) -> Optional[int]:
     return C.c_void_p(stream.cuda_stream)
 
 
-def encode(w16: np.ndarray, group: int, nbits: int, budget: int, ratio_T: float = 4.0) -> Dict:
-    """Run the library's host encoder on an fp16 matrix; returns the unpacked fields."""
+def encode(w16: np.ndarray, group: int, nbits: int, budget: int, ratio_T: float = 4.0,
+           post_per_row: int = 0) -> Dict:
+    """Run the library's host encoder on an fp16 matrix; returns the unpacked
+    fields.  post_per_row = k > 0: k post-grid entries per row, budget caps the
+    pre-grid guard only."""
     w = np.ascontiguousarray(w16, dtype=np.float16)
     R, Cc = w.shape
     G = Cc // group
+    cap = budget + R * post_per_row
     out = dict(
         q=np.empty((R, Cc), np.uint8), planes=np.empty((nbits - 2, R, Cc), np.uint8),
         lo=np.empty((R, G), np.float16), s=np.empty((R, G), np.float16),
-        row_ptr=np.empty(R + 1, np.int32), col=np.empty(budget, np.int32),
-        val=np.empty(budget, np.float16))
+        row_ptr=np.empty(R + 1, np.int32), col=np.empty(cap, np.int32),
+        val=np.empty(cap, np.float16))
     n_pre = C.c_int64(0)
     p = lambda a: a.ctypes.data_as(C.c_void_p)
-    st = lib().stagq_encode(p(w), R, Cc, group, nbits, budget, float(ratio_T), p(out["q"]),
-                            p(out["planes"]) if nbits > 2 else None, p(out["lo"]), p(out["s"]),
-                            p(out["row_ptr"]), p(out["col"]) if budget else None,
-                            p(out["val"]) if budget else None, C.byref(n_pre))
+    st = lib().stagq_encode(p(w), R, Cc, group, nbits, budget, float(ratio_T), int(post_per_row),
+                            p(out["q"]), p(out["planes"]) if nbits > 2 else None, p(out["lo"]),
+                            p(out["s"]), p(out["row_ptr"]), p(out["col"]) if cap else None,
+                            p(out["val"]) if cap else None, C.byref(n_pre))
     check(st, "stagq_encode")
+    nnz = int(out["row_ptr"][-1])
+    out["col"], out["val"] = out["col"][:nnz], out["val"][:nnz]
     out.update(group=group, nbits=nbits, n_pre=int(n_pre.value))
     return out
 

@@ -312,14 +312,16 @@ int stagq_unpack_host(const void* image, size_t image_bytes, stagq_info* shape, 
 // post-grid guard on the largest |w - (lo + s q)| over the matrix (ties by flat
 // index), sign planes skipping held-out entries and zero-step groups.
 int stagq_encode(const uint16_t* w16, int32_t rows, int32_t cols, int32_t group, int32_t nbits,
-                 int64_t budget, double ratio_T, uint8_t* q, uint8_t* planes, uint16_t* lo16,
-                 uint16_t* s16, int32_t* row_ptr, int32_t* col, uint16_t* val, int64_t* n_pre_out) {
+                 int64_t budget, double ratio_T, int32_t post_per_row, uint8_t* q, uint8_t* planes,
+                 uint16_t* lo16, uint16_t* s16, int32_t* row_ptr, int32_t* col, uint16_t* val,
+                 int64_t* n_pre_out) {
   if (rows < 0 || cols <= 0 || group <= 0 || cols % group || nbits < 2 || nbits > kMaxBits)
     return STAGQ_ESHAPE;
   const int64_t R = rows, C = cols, g = group, G = C / g, n = R * C;
   if (budget < 0 || budget > n || budget >= (int64_t(1) << 31)) return STAGQ_EINVAL;
+  if (post_per_row < 0 || budget + R * int64_t(post_per_row) >= (int64_t(1) << 31)) return STAGQ_EINVAL;
   if (n > 0 && (!w16 || !q || !lo16 || !s16 || (nbits > 2 && !planes))) return STAGQ_EINVAL;
-  if (!row_ptr || (budget > 0 && (!col || !val))) return STAGQ_EINVAL;
+  if (!row_ptr || (budget + R * int64_t(post_per_row) > 0 && (!col || !val))) return STAGQ_EINVAL;
 
   std::vector<uint8_t> held(size_t(n), 0);
   // 1. pre-grid guard: one candidate per group at most.
@@ -377,8 +379,30 @@ int stagq_encode(const uint16_t* w16, int32_t rows, int32_t cols, int32_t group,
     }
   });
 
-  // 4. post-grid guard: the budget left, on the largest two-bit residuals.
-  const int64_t n_post = budget - n_pre;
+  // 4. post-grid guard: the budget left on the largest two-bit residuals of
+  //    the matrix, or the post_per_row largest of every row.
+  const int64_t n_post = post_per_row ? 0 : budget - n_pre;
+  if (post_per_row > 0) {
+    struct Res { double r; int64_t c; };
+    parallel_for(R, [&](int64_t a, int64_t b) {
+      std::vector<Res> v;
+      for (int64_t r = a; r < b; r++) {
+        v.clear();
+        for (int64_t c = 0; c < C; c++) {
+          const int64_t i = r * C + c;
+          if (held[size_t(i)]) continue;
+          const int64_t grp = r * G + c / g;
+          const double rec = half_to_double(lo16[grp]) + half_to_double(s16[grp]) * q[i];
+          v.push_back(Res{fabs(half_to_double(w16[i]) - rec), c});
+        }
+        const size_t k = std::min<size_t>(size_t(post_per_row), v.size());
+        std::partial_sort(v.begin(), v.begin() + k, v.end(), [](const Res& x, const Res& y) {
+          return x.r > y.r || (x.r == y.r && x.c < y.c);
+        });
+        for (size_t j = 0; j < k; j++) held[size_t(r * C + v[j].c)] = 1;
+      }
+    });
+  }
   if (n_post > 0) {
     struct Res { double r; int64_t flat; };
     auto by_res = [](const Res& x, const Res& y) {
@@ -453,7 +477,9 @@ int stagq_encode(const uint16_t* w16, int32_t rows, int32_t cols, int32_t group,
     row_ptr[r + 1] = int32_t(e);
   }
   if (n_pre_out) *n_pre_out = n_pre;
-  return e == budget ? STAGQ_OK : STAGQ_EINVAL;
+  // (a global post-grid guard fills the budget exactly; per row, every row
+  // gives min(k, entries left in the row))
+  return post_per_row || e == budget ? STAGQ_OK : STAGQ_EINVAL;
 }
 
 }  // extern "C"

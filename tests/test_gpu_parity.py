@@ -62,7 +62,7 @@ def _encoded(workload, mname):
     wl = WORKLOADS[workload]
     mat = [m for m in wl.matrices if m.name == mname][0]
     w, x = synth_matrix(mat.rows, mat.cols, wl.dist, mat.seed)
-    F = oracle.encode(w, wl.group, wl.nbits, wl.frac, wl.ratio_T)
+    F = oracle.encode(w, wl.group, wl.nbits, wl.frac, wl.ratio_T, post_per_row=wl.post_per_row)
     return F, x
 
 
@@ -95,6 +95,18 @@ SWEEP = [m.name for m in WORKLOADS["layer_sweep"].matrices if m.name != "lm_head
 def test_workload_parity(pwo, workload, mname):
     F, x = _encoded(workload, mname)
     _check(pwo, F, x, WORKLOADS[workload].bits, f"{workload}/{mname}")
+
+
+@pytest.mark.parametrize("mname", [m.name for m in WORKLOADS["mlp_rows"].matrices])
+def test_per_row_workload_csr_and_fixed_slots(pwo, mname):
+    """The MLP shapes at full size with 4 post-grid entries per row: the side
+    record as CSR and in fixed per-row slots (W = the fullest row), both to
+    the parity bar with codes bit-exact."""
+    F, x = _encoded("mlp_rows", mname)
+    for slots in (0, -1):
+        m, _ = _check(pwo, F, x, WORKLOADS["mlp_rows"].bits, f"mlp_rows/{mname} slots={slots}", side_slots=slots)
+        assert m.side_slots == (0 if slots == 0 else int(np.diff(F.row_ptr).max()))
+        del m
 
 
 @pytest.mark.parametrize("mname", SWEEP)

@@ -27,12 +27,14 @@ def test_header_symbols_are_exported():
         assert getattr(lib, name) is not None
 
 
+@pytest.mark.parametrize("post_per_row", [0, 3])
 @pytest.mark.parametrize("shape", [(256, 512, 64, 4, 0.005), (33, 384, 32, 6, 0.02), (5, 1024, 128, 8, 0.01)])
-def test_library_encoder_matches_oracle(shape):
+def test_library_encoder_matches_oracle(shape, post_per_row):
     R, Cc, g, N, frac = shape
     w, _ = synth_matrix(R, Cc, "normal_outliers", 17)
-    F = oracle.encode(w, g, N, frac)
-    E = pwo.encode(w, g, N, F.nnz)
+    F = oracle.encode(w, g, N, frac, post_per_row=post_per_row)
+    E = pwo.encode(w, g, N, oracle.budget(frac, R, Cc) if post_per_row else F.nnz, post_per_row=post_per_row)
+    assert E["n_pre"] == F.n_pre and E["row_ptr"][-1] == F.nnz
     for k in ("q", "planes", "row_ptr", "col"):
         assert np.array_equal(getattr(F, k), E[k]), k
     for k in ("lo", "s", "val"):

@@ -436,3 +436,36 @@ def test_codebook_choice_matches_exact_brute_force(frac):
             best = min(losses)
             assert losses[int(F.idx[r, gi])] == best
             assert int(F.idx[r, gi]) == losses.index(best)
+
+
+def test_per_row_post_grid_pick_by_brute_force():
+    """encode(..., post_per_row=k): the pre-grid guard takes at most the budget
+    (ratio criterion), then every row holds out the k entries with the largest
+    |w - (lo + s q)| among those left, lowest column first on ties; written out
+    row by row in plain Python against the stored pairs and codes."""
+    w, _ = synth_matrix(12, 256, "normal_outliers", 21)
+    k = 3
+    F = oracle.encode(w, 64, 4, 0.005, post_per_row=k)
+    K = oracle.budget(0.005, 12, 256)
+    assert 0 < F.n_pre <= K and F.n_post == 12 * k
+    assert F.nnz == F.n_pre + F.n_post
+    # the pre-grid entries: the ratio criterion, ranked by ratio, capped at K
+    cands = []
+    for r in range(12):
+        for gi in range(4):
+            seg = [abs(float(v)) for v in w[r, gi * 64:(gi + 1) * 64]]
+            j = seg.index(max(seg))
+            second = max(seg[:j] + seg[j + 1:])
+            if seg[j] > 4 * second:
+                cands.append((-(seg[j] / second) if second else -np.inf, r * 256 + gi * 64 + j))
+    pre = {flat for _, flat in sorted(cands)[:K]}
+    for r in range(12):
+        res = []
+        for c in range(256):
+            if r * 256 + c in pre:
+                continue
+            lo, s = float(F.lo[r, c // 64]), float(F.s[r, c // 64])
+            res.append((abs(float(w[r, c]) - (lo + s * int(F.q[r, c]))), c))
+        res.sort(key=lambda t: (-t[0], t[1]))
+        want = {c for _, c in res[:k]} | {f - r * 256 for f in pre if f // 256 == r}
+        assert set(np.nonzero(F.mask[r])[0].tolist()) == want, r

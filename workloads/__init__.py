@@ -56,6 +56,7 @@ class Workload:
     bits: Tuple[int, ...]
     ratio_T: float = 4.0
     note: str = field(default="")
+    post_per_row: int = 0   # k > 0: k post-grid entries per row (frac caps the pre-grid guard)
 
 
 WORKLOADS = {
@@ -69,6 +70,12 @@ WORKLOADS = {
         "mlp", (Matrix("gate_up", 14336, 4096, 0), Matrix("down", 4096, 14336, 1)),
         "student_t", 128, 4, 0.001, (2, 3, 4),
         note="Llama-3.1-8B MLP: gate/up 14336x4096, down 4096x14336"),
+    "mlp_rows": Workload(
+        "mlp_rows", (Matrix("gate_up", 14336, 4096, 0), Matrix("down", 4096, 14336, 1)),
+        "student_t", 128, 4, 0.001, (2, 3, 4),
+        note="the MLP shapes with 4 post-grid entries per row (about the same side-record size "
+             "as 0.1% of the weights), the record in fixed per-row slots or CSR",
+        post_per_row=4),
     "phi4_mlp": Workload(
         "phi4_mlp", (Matrix("gate_up", 17920, 5120, 0), Matrix("down", 5120, 17920, 1)),
         "student_t", 128, 6, 0.002, (2, 3, 4, 5, 6),
