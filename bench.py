@@ -287,7 +287,7 @@ def main():
                     help="also run 5 device-to-device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 (the GEMV path has "
+        print("bench.py: the GEMV runs on one GPU only; --gpus must be 1 (the GEMV path has "
               "no multi-GPU leg).", file=sys.stderr)
         sys.exit(2)
 

@@ -38,6 +38,12 @@
 //    segmented scan, so rows with many held-out weights cost no more than the
 //    rest: on an extra wave of the workgroup while the others stream (grids of
 //    two or more workgroups per CU), else by all waves after the main loop.
+//    With fixed per-row slots instead of CSR, every slot's address is known at
+//    once: a lane sums its row's slots, and no row_ptr is read.
+//  * Issue order: all kernel arguments arrive in one batch of scalar loads, and
+//    wave priorities favour the side-record wave, then waves in their prologue,
+//    then waves in their first steps, so the waves behind catch up.
+//  * Optionally the row sums are stored rounded to fp16.
 //  * Row sums: the 4 S lane partials of a row, then its corrections, are added
 //    in a fixed order (no atomics), so y is bitwise reproducible for a given
 //    shape and M.
