@@ -201,7 +201,7 @@ def sweep(args):
                 b = base.bytes_read[M]
                 entry["bits"][str(M)] = {"us": round(us, 3), "bytes": int(b), "gbps": round(b / us / 1e3, 1),
                                          "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2),
-                                         "launch": pwo.plan_gemv(mat.rows, mat.cols, wl.group, wl.nbits, M)}
+                                         "launch": base.plan(M)}
             if wname == "mlp":
                 # the same GEMVs with the inverse AWQ scale applied to x (stagq_gemv_scaled)
                 sc = torch.from_numpy(np.full(mat.cols, 0.5, np.float16).view(np.int16)).view(torch.float16).to(dev)
@@ -413,7 +413,7 @@ def main():
             "pct_peak": round(100.0 * bytes_alg[M] / (mean * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
             "a100_stagq_us": A100_STAGQ_US[M],
             "read_ceiling": ceiling.get(M),
-            "launch": pwo.plan_gemv(R, Cc, wl.group, wl.nbits, M),
+            "launch": base.plan(M),
         }
     step_bytes = sum(bytes_alg.values())
     value = step_bytes * K / wall / 1e9

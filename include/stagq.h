@@ -206,8 +206,10 @@ int stagq_gemv_f16(stagq_handle h, const void* x, const void* x_scale, void* y, 
 int stagq_decode_codes(stagq_handle h, int bits, uint8_t* codes, void* hip_stream);
 
 /*
- * Launch shape the GEMV uses for a matrix of this shape at precision bits (on
- * the current device, or assuming 256 compute units when none is present):
+ * Launch shape the GEMV uses for a matrix of this shape, side-record size nnz
+ * and side-record format (side_slots as in stagq_fields, resolved: 0 CSR, W > 0
+ * fixed slots) at precision bits (on the current device, or assuming 256
+ * compute units when none is present):
  * out[0] workgroups (one per 16-row block), out[1] threads per workgroup,
  * out[2] waves per workgroup that stream the main stream, out[3] steps per
  * such wave (a step is 16 rows x 4 tile columns of 128), out[4] rows per
@@ -215,8 +217,8 @@ int stagq_decode_codes(stagq_handle h, int bits, uint8_t* codes, void* hip_strea
  * wave of each workgroup (else 0), out[7] steps of loads in flight per wave.
  * out is host int32[8].  Pure host logic.
  */
-int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int bits,
-                    int32_t* out);
+int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int64_t nnz,
+                    int32_t side_slots, int bits, int32_t* out);
 
 /*
  * Streaming-read ceiling (measurement aid, not part of the method): read bytes

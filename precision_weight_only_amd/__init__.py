@@ -66,11 +66,12 @@ def encode(w16: np.ndarray, group: int, nbits: int, budget: int, ratio_T: float 
     return out
 
 
-def plan_gemv(rows: int, cols: int, group: int, nbits: int, bits: int) -> Dict[str, int]:
+def plan_gemv(rows: int, cols: int, group: int, nbits: int, bits: int, nnz: int = 0,
+              side_slots: int = 0) -> Dict[str, int]:
     """Launch shape the library picks for this GEMV (workgroups, threads, ...)."""
     out = (C.c_int32 * 8)()
-    check(lib().stagq_plan_gemv(rows, cols, group, nbits, bits, C.cast(out, C.c_void_p)),
-          "stagq_plan_gemv")
+    check(lib().stagq_plan_gemv(rows, cols, group, nbits, int(nnz), int(side_slots), bits,
+                                C.cast(out, C.c_void_p)), "stagq_plan_gemv")
     keys = ("grid", "threads", "waves", "steps_per_wave", "rows_per_group", "lds_bytes",
             "side_wave", "depth")
     return dict(zip(keys, list(out)))
@@ -166,6 +167,10 @@ class StagQMatrix:
         info = Info()
         check(lib().stagq_query(h, C.byref(info)), "stagq_query")
         return cls(h, buf, info)
+
+    def plan(self, bits: int) -> Dict[str, int]:
+        """Launch shape of this matrix's GEMV at precision bits."""
+        return plan_gemv(self.rows, self.cols, self.group, self.nbits, bits, self.nnz, self.side_slots)
 
     def clone_to(self, buffer) -> "StagQMatrix":
         """Handle for another device buffer holding a copy of this image."""

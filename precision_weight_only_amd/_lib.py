@@ -69,7 +69,8 @@ def _load() -> C.CDLL:
         "stagq_encode": (C.c_int, [P, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int64,
                                    C.c_double, C.c_int32, P, P, P, P, P, P, P, C.POINTER(C.c_int64)]),
         "stagq_unpack_host": (C.c_int, [P, C.c_size_t, C.POINTER(Info), P, P, P, P, P, P, P]),
-        "stagq_plan_gemv": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int, P]),
+        "stagq_plan_gemv": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int64, C.c_int32,
+                                      C.c_int, P]),
         "stagq_stream_read": (C.c_int, [P, C.c_size_t, P, P]),
     }
     for name, (res, args) in sig.items():

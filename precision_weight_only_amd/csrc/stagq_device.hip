@@ -983,23 +983,30 @@ static size_t lds_layout(int C, int S, bool cb, dev::GemvParams* prm) {
 }
 
 // Launch shape: one workgroup per 16-row block, S waves splitting the row's
-// groups of four tile columns.  S is the smallest count that puts about two
-// waves on every SIMD (8 per CU), within [ceil(groups / 4), min(16, groups)]
-// (a wave stages the x of at most 4 steps).  With at least two workgroups per
-// CU the side record goes to an extra wave (its latency then hides behind
-// other workgroups; with fewer it would sit on the critical path), and up to
-// 4 bits each wave then takes the most steps it can (measured on 14336 x 4096:
-// 7.2 / 8.2 us at 2 / 3 bits against 7.6 / 8.6 with two waves per SIMD; at 4
-// bits, with two steps in flight, equal).
+// groups of four tile columns, and the side record on an extra wave.  Up to 4
+// bits each wave takes the most steps it can (S = ceil(groups / 4): a wave
+// stages the x of at most 4 steps; measured on 14336 x 4096: 7.2 / 8.2 us at
+// 2 / 3 bits against 7.6 / 8.6 with two waves per SIMD; at 4 bits, with two
+// steps in flight, equal); from 5 bits S is the smallest count that puts
+// about two waves on every SIMD (8 per CU), within [ceil(groups / 4),
+// min(15, groups)].  The side record goes to the extra wave on grids of two or
+// more workgroups per CU, when it is light (at most 128 entries per block on
+// average) and when it sits in fixed slots (no dependent loads); a heavy CSR
+// record on a smaller grid is applied by all waves after the loop, since the
+// side wave's chain of dependent loads would then set the launch's end
+// (measured in one session, 2 / 3 / 4 bits: 4096 x 4096 with 65 entries per
+// block, 4.65 / 4.97 / 5.04 us on the extra wave against 4.81 / 5.19 / 5.45;
+// 5120 x 17920 with 573, 12.9 / 14.4 / 17.8 against 11.9 / 15.8 / 15.9).
 // STAGQ_WAVES and STAGQ_SIDE override the choices (tuning); STAGQ_FLAG_SPINS
 // sets the side-record wave's spin limit (testing its global-x fallback).
+constexpr int kLightSide = 128;   // side-record entries per block, on average, that the extra wave takes
 static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   const int T = h.cols / kTileCols;
   const int Q = (T + 3) / 4;
   const int nblk = h.blocks;
   if (nblk <= 0) return false;
   const int cus = device_cus();
-  bool side = nblk >= 2 * cus;
+  bool side = nblk >= 2 * cus || h.side_slots > 0 || h.nnz <= int64_t(kLightSide) * nblk;
   const int side_env = env_int("STAGQ_SIDE", -1);
   if (side_env == 0 || side_env == 1) side = side_env == 1;
   const int smin = (Q + dev::kXChunks - 1) / dev::kXChunks;
@@ -1175,11 +1182,11 @@ int stagq_gemv_f16(stagq_handle h, const void* x, const void* x_scale, void* y, 
   return gemv_call(h, x, x_scale, x_scale != nullptr, y, true, bits, hip_stream);
 }
 
-int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int bits,
-                    int32_t* out) {
+int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int64_t nnz,
+                    int32_t side_slots, int bits, int32_t* out) {
   if (!out) return STAGQ_EINVAL;
   ImageHeader H;
-  if (!layout(rows, cols, group, nbits, 0, &H)) return STAGQ_ESHAPE;
+  if (!layout(rows, cols, group, nbits, nnz, &H, false, side_slots)) return STAGQ_ESHAPE;
   if (bits < 2 || bits > nbits) return STAGQ_EBITS;
   LaunchCfg c;
   if (!plan_gemv(H, bits, &c)) return STAGQ_ESHAPE;

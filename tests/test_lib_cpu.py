@@ -149,8 +149,8 @@ def test_validation_errors():
 
 def test_unsupported_shapes():
     for (R, Cc, g, N) in [(4, 100, 50, 4), (4, 256, 16, 4), (4, 256, 128, 9), (4, 256, 128, 1)]:
-        assert pwo.lib().stagq_plan_gemv(R, Cc, g, N, 2, (C.c_int32 * 8)()) == -3
-    assert pwo.lib().stagq_plan_gemv(4, 256, 128, 4, 5, (C.c_int32 * 8)()) == -2
+        assert pwo.lib().stagq_plan_gemv(R, Cc, g, N, 0, 0, 2, (C.c_int32 * 8)()) == -3
+    assert pwo.lib().stagq_plan_gemv(4, 256, 128, 4, 0, 0, 5, (C.c_int32 * 8)()) == -2
 
 
 def test_strerror_covers_every_status():
@@ -160,19 +160,26 @@ def test_strerror_covers_every_status():
 
 def test_launch_plan_shapes():
     """Launch shapes for a 256-CU device (the host-only default): one
-    workgroup per 16-row block; with two or more blocks per CU the side record
-    runs on an extra wave and, up to 4 bits, each wave takes the most steps it
-    can (4, as x is staged for at most 4 steps)."""
-    def plan(R, Cc, bits, g=128, N=4):
+    workgroup per 16-row block; the side record on an extra wave with two or
+    more blocks per CU, a light record (at most 128 entries per block on
+    average) or fixed slots, else after the loop; up to 4 bits each wave takes
+    the most steps it can (4, as x is staged for at most 4 steps)."""
+    def plan(R, Cc, bits, g=128, N=4, nnz=0, slots=0):
         out = (C.c_int32 * 8)()
-        assert pwo.lib().stagq_plan_gemv(R, Cc, g, N, bits, out) == 0
+        assert pwo.lib().stagq_plan_gemv(R, Cc, g, N, nnz, slots, bits, out) == 0
         return dict(grid=out[0], threads=out[1], S=out[2], steps=out[3], side=out[6])
     p2, p4, p5 = plan(14336, 4096, 2), plan(14336, 4096, 4), plan(14336, 4096, 5, N=6)
     assert (p2["grid"], p2["S"], p2["steps"], p2["side"], p2["threads"]) == (896, 2, 4, 1, 192)
     assert (p4["S"], p4["steps"], p4["threads"]) == (2, 4, 192)
     assert (p5["S"], p5["steps"], p5["threads"]) == (3, 3, 256)
     d = plan(4096, 14336, 2)
-    assert (d["grid"], d["S"], d["side"], d["threads"]) == (256, 8, 0, 512)
+    assert (d["grid"], d["S"], d["side"], d["threads"]) == (256, 7, 1, 512)   # no side record: light
+    dh = plan(4096, 14336, 2, nnz=58720)           # 229 entries per block: after the loop
+    assert (dh["S"], dh["side"], dh["threads"]) == (8, 0, 512)
+    assert plan(4096, 14336, 2, nnz=32768)["side"] == 1 and plan(4096, 14336, 2, nnz=32769)["side"] == 0
+    assert plan(4096, 14336, 3, nnz=58720, slots=30)["side"] == 1
+    d6 = plan(5120, 17920, 6, N=6, nnz=183501)     # 320 blocks, 35 groups of four tile columns
+    assert (d6["grid"], d6["S"], d6["side"], d6["threads"]) == (320, 9, 0, 576)
     lm = plan(128256, 4096, 3)
     assert (lm["grid"], lm["S"], lm["side"]) == (8016, 2, 1)
 
