@@ -918,6 +918,7 @@ __global__ void __launch_bounds__(256) codes_kernel(const CodesParams p) {
 struct LaunchCfg {
   int S, grid, nt_max;
   bool side;                    // side record on an extra wave (SIDE mode)
+  bool deep;                    // the deeper depth table (see kDepthMany)
   size_t lds;
   dev::GemvParams prm;
 };
@@ -949,16 +950,18 @@ static int env_int(const char* name, int dflt) {
   return e ? atoi(e) : dflt;
 }
 
-// Steps of loads in flight per wave, per precision, for the side-record-wave
-// grids (many blocks) and the in-workgroup ones.  Shallow on purpose: with
-// two to four waves per SIMD the chip holds enough bytes in flight, and
-// deeper per-wave queues only delay every wave's first data.  Measured: depth
-// 2 beats 3 and 4 at 2-3 bits (14336 x 4096, 4096 x 14336); at 4 bits depth 2
-// beats 1 on the many-block grids (17920 x 5120: 12.5 against 13.4 us; equal
-// on 14336 x 4096) but loses on 5120 x 17920 (17.3 against 15.7 us); from 5
-// bits depth 1 wins.
-constexpr int kDepthSide[9] = {0, 0, 2, 2, 2, 1, 1, 1, 1};
-constexpr int kDepthInWg[9] = {0, 0, 2, 2, 1, 1, 1, 1, 1};
+// Steps of loads in flight per wave, per precision: with the side-record wave
+// on grids of two or more workgroups per CU or with a light (or fixed-slot)
+// record, and otherwise (a heavy record on a smaller grid, or the record
+// applied after the loop).  Shallow on purpose: with two to four waves per SIMD
+// the chip holds enough bytes in flight, and deeper per-wave queues only delay
+// every wave's first data.  Measured: depth 2 beats 3 and 4 at 2-3 bits
+// (14336 x 4096, 4096 x 14336); at 4 bits depth 2 beats 1 on 17920 x 5120
+// (12.5 against 13.4 us), 14336 x 4096 (8.5 against 8.8) and 4096 x 4096 with
+// a light record (5.05 against 6.44) but loses on 5120 x 17920 with a heavy one
+// (16.9 against 14.7 us); from 5 bits depth 1 wins.
+constexpr int kDepthMany[9] = {0, 0, 2, 2, 2, 1, 1, 1, 1};
+constexpr int kDepthFew[9] = {0, 0, 2, 2, 1, 1, 1, 1, 1};
 constexpr int kMaxWaves = 16;   // waves per workgroup (incl. a side-record wave): __launch_bounds__(1024)
 
 // LDS carve-up: per tile (padded tile columns, plus a spare tile) 64 dwords
@@ -989,14 +992,17 @@ static size_t lds_layout(int C, int S, bool cb, dev::GemvParams* prm) {
 // 2 / 3 bits against 7.6 / 8.6 with two waves per SIMD; at 4 bits, with two
 // steps in flight, equal); from 5 bits S is the smallest count that puts
 // about two waves on every SIMD (8 per CU), within [ceil(groups / 4),
-// min(15, groups)].  The side record goes to the extra wave on grids of two or
-// more workgroups per CU, when it is light (at most 128 entries per block on
-// average) and when it sits in fixed slots (no dependent loads); a heavy CSR
-// record on a smaller grid is applied by all waves after the loop, since the
-// side wave's chain of dependent loads would then set the launch's end
-// (measured in one session, 2 / 3 / 4 bits: 4096 x 4096 with 65 entries per
-// block, 4.65 / 4.97 / 5.04 us on the extra wave against 4.81 / 5.19 / 5.45;
-// 5120 x 17920 with 573, 12.9 / 14.4 / 17.8 against 11.9 / 15.8 / 15.9).
+// min(15, groups)].  The side record goes to the extra wave except for a
+// heavy CSR record (more than 128 entries per block on average) on a grid of
+// fewer than two workgroups per CU at 2 bits: there the main waves finish
+// soonest and the side wave's chain of dependent loads would set the launch's
+// end, so all waves apply the record after the loop.  Fixed slots have no
+// such chain.  Measured in one session (us at 2 / 3 / 4 / 5 / 6 bits, extra
+// wave against after the loop): 4096 x 4096, 65 entries per block,
+// 4.65 / 4.97 / 5.04 against 4.81 / 5.19 / 5.45; 5120 x 17920, 573 per block,
+// 11.7 / 13.7 / 14.7 / 19.9 / 21.3 against 11.4 / 15.9 / 15.8 / 20.9 / 22.9
+// (4 bits with depth 1); 4096 x 14336, 229 per block, 7.56 / 7.95 / 8.82
+// against 7.46 / 8.32 / 9.69.
 // STAGQ_WAVES and STAGQ_SIDE override the choices (tuning); STAGQ_FLAG_SPINS
 // sets the side-record wave's spin limit (testing its global-x fallback).
 constexpr int kLightSide = 128;   // side-record entries per block, on average, that the extra wave takes
@@ -1006,7 +1012,9 @@ static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   const int nblk = h.blocks;
   if (nblk <= 0) return false;
   const int cus = device_cus();
-  bool side = nblk >= 2 * cus || h.side_slots > 0 || h.nnz <= int64_t(kLightSide) * nblk;
+  const bool many = nblk >= 2 * cus;
+  const bool light = h.side_slots > 0 || h.nnz <= int64_t(kLightSide) * nblk;
+  bool side = many || light || bits >= 3;
   const int side_env = env_int("STAGQ_SIDE", -1);
   if (side_env == 0 || side_env == 1) side = side_env == 1;
   const int smin = (Q + dev::kXChunks - 1) / dev::kXChunks;
@@ -1022,6 +1030,7 @@ static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   if (S < smin || S > smax) return false;
   c->S = S;
   c->side = side;
+  c->deep = many || light;
   c->grid = nblk;
   c->nt_max = (Q + S - 1) / S;
   c->lds = lds_layout(h.cols, S, h.codebook != 0, &c->prm);
@@ -1048,7 +1057,8 @@ static hipError_t launch_gemv(const LaunchCfg& c, hipStream_t st) {
 
 template <int M, int GU>
 static hipError_t launch_gemv_d(const LaunchCfg& c, hipStream_t st) {
-  return c.side ? launch_gemv<M, GU, kDepthSide[M]>(c, st) : launch_gemv<M, GU, kDepthInWg[M]>(c, st);
+  // (the in-workgroup mode only runs on smaller grids)
+  return c.deep && c.side ? launch_gemv<M, GU, kDepthMany[M]>(c, st) : launch_gemv<M, GU, kDepthFew[M]>(c, st);
 }
 
 template <int M>
@@ -1191,7 +1201,7 @@ int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, in
   LaunchCfg c;
   if (!plan_gemv(H, bits, &c)) return STAGQ_ESHAPE;
   out[0] = c.grid; out[1] = 64 * (c.S + (c.side ? 1 : 0)); out[2] = c.S; out[3] = c.nt_max;
-  out[4] = kBlockRows; out[5] = int32_t(c.lds); out[6] = c.side ? 1 : 0; out[7] = c.side ? kDepthSide[bits] : kDepthInWg[bits];
+  out[4] = kBlockRows; out[5] = int32_t(c.lds); out[6] = c.side ? 1 : 0; out[7] = c.deep && c.side ? kDepthMany[bits] : kDepthFew[bits];
   return STAGQ_OK;
 }
 

@@ -160,10 +160,10 @@ def test_strerror_covers_every_status():
 
 def test_launch_plan_shapes():
     """Launch shapes for a 256-CU device (the host-only default): one
-    workgroup per 16-row block; the side record on an extra wave with two or
-    more blocks per CU, a light record (at most 128 entries per block on
-    average) or fixed slots, else after the loop; up to 4 bits each wave takes
-    the most steps it can (4, as x is staged for at most 4 steps)."""
+    workgroup per 16-row block; the side record on an extra wave except for a
+    heavy CSR record (over 128 entries per block on average) on a grid of fewer
+    than two blocks per CU at 2 bits; up to 4 bits each wave takes the most
+    steps it can (4, as x is staged for at most 4 steps)."""
     def plan(R, Cc, bits, g=128, N=4, nnz=0, slots=0):
         out = (C.c_int32 * 8)()
         assert pwo.lib().stagq_plan_gemv(R, Cc, g, N, nnz, slots, bits, out) == 0
@@ -178,8 +178,13 @@ def test_launch_plan_shapes():
     assert (dh["S"], dh["side"], dh["threads"]) == (8, 0, 512)
     assert plan(4096, 14336, 2, nnz=32768)["side"] == 1 and plan(4096, 14336, 2, nnz=32769)["side"] == 0
     assert plan(4096, 14336, 3, nnz=58720, slots=30)["side"] == 1
+    assert plan(4096, 14336, 3, nnz=58720)["side"] == 1                  # heavy, small grid: 2 bits only
     d6 = plan(5120, 17920, 6, N=6, nnz=183501)     # 320 blocks, 35 groups of four tile columns
-    assert (d6["grid"], d6["S"], d6["side"], d6["threads"]) == (320, 9, 0, 576)
+    assert (d6["grid"], d6["S"], d6["side"], d6["threads"]) == (320, 9, 1, 640)
+    out = (C.c_int32 * 8)()                        # steps in flight at 4 bits: 1 on smaller grids, 2 on many
+    assert pwo.lib().stagq_plan_gemv(5120, 17920, 128, 6, 183501, 0, 4, out) == 0 and (out[6], out[7]) == (1, 1)
+    assert pwo.lib().stagq_plan_gemv(14336, 4096, 128, 4, 58720, 0, 4, out) == 0 and (out[6], out[7]) == (1, 2)
+    assert pwo.lib().stagq_plan_gemv(4096, 4096, 128, 4, 16777, 0, 4, out) == 0 and (out[6], out[7]) == (1, 2)
     lm = plan(128256, 4096, 3)
     assert (lm["grid"], lm["S"], lm["side"]) == (8016, 2, 1)
 
