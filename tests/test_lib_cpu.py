@@ -299,3 +299,11 @@ def test_fixed_slot_side_record_validation():
     F0 = oracle.encode(w, 128, 4, 0.0)
     assert pwo.unpack_host(pwo.pack_host(F0, side_slots=-1))["side_slots"] == 0
     assert pwo.unpack_host(pwo.pack_host(F, side_slots=4096))["side_slots"] == 4096
+    # a row fuller than the 4096-slot limit cannot go to slots sized for it
+    wb, _ = synth_matrix(1, 16384, "student_t", 20)
+    Fb = oracle.encode(wb, 128, 4, 0.3)
+    assert int(np.diff(Fb.row_ptr).max()) > 4096
+    assert pwo.packed_bytes(Fb, side_slots=-1) == 0 and pwo.packed_bytes(Fb) > 0
+    with pytest.raises(pwo.StagQError) as e:
+        pwo.pack_host(Fb, side_slots=-1)
+    assert e.value.status == -4
