@@ -36,8 +36,8 @@
 //    its planes are zero).  The block's entries (contiguous in CSR order) are
 //    spread over the lanes whatever their row and summed per row with a
 //    segmented scan, so rows with many held-out weights cost no more than the
-//    rest: on an extra wave of the workgroup while the others stream (grids of
-//    two or more workgroups per CU), else by all waves after the main loop.
+//    rest: on an extra wave of the workgroup while the others stream, or (a
+//    heavy record on a small grid at 2 bits) by all waves after the main loop.
 //    With fixed per-row slots instead of CSR, every slot's address is known at
 //    once: a lane sums its row's slots, and no row_ptr is read.
 //  * Issue order: all kernel arguments arrive in one batch of scalar loads, and
@@ -557,9 +557,10 @@ __device__ __forceinline__ void side_slots_wave(const GemvParams& p, int blk, in
 }
 
 // The GEMV.  SIDE selects where the side record is applied: by an extra wave
-// of the workgroup (SIDE = 1, for grids with several workgroups per CU, where
-// its latency hides behind other workgroups) or by all waves after the main
-// loop (SIDE = 0).  SC: x is multiplied by the per-channel inverse AWQ scale
+// of the workgroup (SIDE = 1, at the highest wave priority, while the others
+// stream) or by all waves after the main loop (SIDE = 0, for a heavy record on
+// a small grid at 2 bits, where the main waves finish before the extra wave's
+// dependent loads would).  SC: x is multiplied by the per-channel inverse AWQ scale
 // p.xsc as it is staged (each product rounded once to fp16).  CB: the group
 // metadata is a codebook index per group; each wave keeps its own LDS copy of
 // the 256 pairs (1 KB) and looks the pair up once per group.
