@@ -1058,7 +1058,8 @@ static hipError_t launch_gemv(const LaunchCfg& c, hipStream_t st) {
 
 template <int M, int GU>
 static hipError_t launch_gemv_d(const LaunchCfg& c, hipStream_t st) {
-  // (the in-workgroup mode only runs on smaller grids)
+  // (the in-workgroup mode takes the shallower table: it runs for heavy
+  // records on smaller grids, or when forced)
   return c.deep && c.side ? launch_gemv<M, GU, kDepthMany[M]>(c, st) : launch_gemv<M, GU, kDepthFew[M]>(c, st);
 }
 
