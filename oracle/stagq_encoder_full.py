@@ -53,9 +53,16 @@ FE7  Post-grid guard over the entries the pre-grid guard left: under the ratio
     (lowest column on ties); under the gain criterion that error per stored
     bit, b_post = 16 + ceil(log2 C) (an fp16 residual and a column index), the
     three highest of each row kept when above tau.
-FE8  The side record stores the held-out weight itself as fp16 (reading R6 of
-    the main oracle module); the paper's 8-bit codes and fp16 residuals change
-    only how P is stored and are not modelled.  Neither guard has a budget cap.
+FE8  storage "weight": the side record stores the held-out weight itself as
+    fp16 (reading R6 of the main oracle module).  storage "paper": the side-
+    record codes of Appendix E -- a pre-grid entry of the gain criterion is an
+    8-bit symmetric code against one fp16 scale per row (scale = fp16(largest
+    |w| of the row's pre-grid entries / 127), code = w / scale rounded to
+    nearest even and clamped to [-127, 127], value code * scale); a pre-grid
+    entry of the ratio criterion is w in fp16; a post-grid entry is its fp16
+    residual against the two-bit base (value lo + s q + fp16(w - (lo + s q))).
+    The record the GEMV reads holds one fp16 value per entry, so each value is
+    rounded once to fp16.  Neither guard has a budget cap.
 
 Pinned by tests/test_oracle_full_encoder.py: Lloyd fixed points and monotone
 distortion, the rule choice and fallback against brute force through the
@@ -215,15 +222,18 @@ def _fit_pairs(v, E, nbits, lam, lo64, hi64, fallback):
 
 def encode_full(w16: np.ndarray, group: int, nbits: int, E: Optional[np.ndarray] = None,
                 criterion: str = "ratio", T: float = 4.0, tau: float = 1e-8,
-                lam: float = 4.0, fallback: float = 0.1) -> Fields:
+                lam: float = 4.0, fallback: float = 0.1, storage: str = "weight") -> Fields:
     """The full encoder in Figure 3's order.  criterion "ratio": the pre-grid
     guard of section 3.5 with factor T and one post-grid entry per row;
     "gain": Eq. (11) with threshold tau for both guards.  The pair is always
     the codebook metadata of section 3.1; fallback is the ratio of six-bit to
     two-bit error above which the codebooks revert to uniform placement (a
-    tenth in Appendix E).  Returns Fields with .info."""
+    tenth in Appendix E); storage selects how the side record holds its
+    values (FE8).  Returns Fields with .info."""
     if criterion not in ("ratio", "gain"):
         raise ValueError("criterion must be 'ratio' or 'gain'")
+    if storage not in ("weight", "paper"):
+        raise ValueError("storage must be 'weight' or 'paper'")
     w16 = np.asarray(w16)
     if w16.ndim != 2 or w16.dtype != np.float16:
         raise ValueError("encode_full expects a 2-D float16 matrix")
@@ -277,6 +287,7 @@ def encode_full(w16: np.ndarray, group: int, nbits: int, E: Optional[np.ndarray]
             mask[rr, gg, jj[rr, gg]] = True
         info["gain"] = gain
     n_pre = int(mask.sum())
+    pre_mask = mask.reshape(R, C).copy()
 
     # 2. Pair fit over the group with its pre-grid entry clipped to the next
     #    value inward (= clamped to the range of the others), section 3.1.
@@ -321,9 +332,24 @@ def encode_full(w16: np.ndarray, group: int, nbits: int, E: Optional[np.ndarray]
         planes[k - 3] = bk
         rec = rec + np.where(active, (2.0 * bk - 1.0) * s_f / 2.0 ** (k - 1), 0.0)
 
-    # 6. Side record, CSR by (row, col), the held-out weight itself (FE8).
+    # 6. Side record, CSR by (row, col): the held-out weight itself, or the
+    #    paper's codes (FE8).
     mask2 = mask.reshape(R, C)
     rr, cc = np.nonzero(mask2)
+    P = w.copy()
+    if storage == "paper":
+        base = (lo_f + s_f * q).reshape(R, C)                  # exact
+        r16 = (w - base).astype(np.float16).astype(np.float64)  # fp16 residual
+        P = np.where(post, base + r16, P)
+        if criterion == "gain":
+            for r in range(R):
+                cols = np.nonzero(pre_mask[r])[0]
+                if cols.size == 0:
+                    continue
+                scale = float(np.float16(np.abs(w[r, cols]).max() / 127.0))
+                code = np.clip(np.rint(w[r, cols] / scale), -127, 127) if scale > 0 else 0.0 * cols
+                P[r, cols] = code * scale
+    val = P[rr, cc].astype(np.float16)
     row_ptr = np.zeros(R + 1, dtype=np.int64)
     np.add.at(row_ptr, rr + 1, 1)
     row_ptr = np.cumsum(row_ptr).astype(np.int32)
@@ -331,5 +357,5 @@ def encode_full(w16: np.ndarray, group: int, nbits: int, E: Optional[np.ndarray]
         rows=R, cols=C, group=group, nbits=nbits,
         q=q.reshape(R, C).astype(np.uint8), planes=planes.reshape(nbits - 2, R, C),
         lo=lo16, s=s16, mask=mask2, row_ptr=row_ptr, col=cc.astype(np.int32),
-        val=w16[rr, cc].astype(np.float16), n_pre=n_pre, n_post=n_post,
+        val=val, n_pre=n_pre, n_post=n_post,
         idx=idx, cb_log2s=cb_log2s, cb_ratio=cb_ratio, info=info)

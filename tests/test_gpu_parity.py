@@ -421,11 +421,12 @@ def test_fp16_output_gemv(pwo, side, monkeypatch):
     torch.cuda.synchronize()
 
 
-@functools.lru_cache(maxsize=4)
-def _full_encoded(case, criterion):
+@functools.lru_cache(maxsize=8)
+def _full_encoded(case, criterion, storage="weight"):
     R, Cc, g, N, dist, seed = case
     w, x = synth_matrix(R, Cc, dist, seed)
-    return oracle.encode_full(w, g, N, E=synth_channel_energy(Cc, seed), criterion=criterion, tau=1e-4), x
+    return oracle.encode_full(w, g, N, E=synth_channel_energy(Cc, seed), criterion=criterion, tau=1e-4,
+                              storage=storage), x
 
 
 @pytest.mark.parametrize("criterion", ["ratio", "gain"])
@@ -445,6 +446,9 @@ def test_full_encoder_workload(pwo, criterion, side, monkeypatch):
         m, _ = _check(pwo, F, x, (2, case[3]), f"full encoder {criterion} {case} side={side} slots",
                       side_slots=-1)
         assert m.side_slots == int(np.diff(F.row_ptr).max())
+        # the pages' side-record codes (8-bit pre-grid codes, fp16 residuals)
+        Fp, _ = _full_encoded(case, criterion, "paper")
+        _check(pwo, Fp, x, (2, case[3]), f"full encoder {criterion} {case} side={side} paper codes")
 
 
 @pytest.mark.parametrize("side", ["0", "1"])

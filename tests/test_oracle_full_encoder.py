@@ -378,3 +378,56 @@ def test_channel_energy_recipe():
     # 20 lifted channels sit near ln 100 = 4.6 in log space, the body near 0:
     # about 17 of the 20 and 1 of the body lie above 3.5
     assert 10 <= int((np.log(e) > 3.5).sum()) <= 25
+
+
+@pytest.mark.parametrize("criterion", ["ratio", "gain"])
+def test_paper_side_record_codes(criterion):
+    """Appendix E's side-record codes (reading FE8), entry by entry in plain
+    Python: post-grid entries hold the two-bit base plus the fp16 residual;
+    pre-grid entries hold w in fp16 under the ratio criterion, and under the
+    gain criterion an 8-bit code times the row's fp16 scale (the largest |w| of
+    the row's pre-grid entries / 127), within half a scale step of w; every
+    value is rounded once to fp16.  Nothing but the recorded values changes."""
+    w, x = synth_matrix(12, 256, "normal_outliers", 23)
+    E = synth_channel_energy(256, 23)
+    Fw = oracle.encode_full(w, 64, 4, E=E, criterion=criterion, tau=1e-5)
+    F = oracle.encode_full(w, 64, 4, E=E, criterion=criterion, tau=1e-5, storage="paper")
+    for k in ("q", "planes", "mask", "row_ptr", "col", "idx"):
+        assert np.array_equal(getattr(F, k), getattr(Fw, k)), k
+    assert np.array_equal(Fw.val, w[Fw.mask])          # storage "weight": w itself
+    if criterion == "ratio":
+        pre = _ratio_pre_grid(w, 64, 4.0)
+    else:
+        hold = F.info["gain"] / oracle.entry_bits(w.size, max(F.n_pre, 1)) > 1e-5
+        pre = np.zeros_like(F.mask)
+        for r in range(12):
+            for gi in range(4):
+                if hold[r, gi]:
+                    seg = [abs(float(v)) for v in w[r, gi * 64:(gi + 1) * 64]]
+                    pre[r, gi * 64 + seg.index(max(seg))] = True
+    n_checked = {"pre": 0, "post": 0}
+    for r in range(12):
+        pre_cols = [c for c in range(256) if pre[r, c]]
+        scale = float(np.float16(max(abs(float(w[r, c])) for c in pre_cols) / 127)) if pre_cols else 0.0
+        for e in range(F.row_ptr[r], F.row_ptr[r + 1]):
+            c = int(F.col[e])
+            wv = float(w[r, c])
+            got = float(F.val[e])
+            if pre[r, c]:
+                if criterion == "ratio":
+                    want = wv
+                else:
+                    code = max(-127, min(127, round(wv / scale)))   # Python round: half to even
+                    want = float(np.float16(code * scale))
+                    assert abs(code * scale - wv) <= scale / 2 + 1e-12
+                n_checked["pre"] += 1
+            else:
+                lo, s = float(F.lo[r, c // 64]), float(F.s[r, c // 64])
+                base = lo + s * int(F.q[r, c])
+                want = float(np.float16(base + float(np.float16(wv - base))))
+                n_checked["post"] += 1
+            assert got == want, (r, c)
+    assert n_checked["pre"] > 0 and n_checked["post"] > 0
+    y = oracle.gemv(F, x, 3)                               # the recorded values are what W_hat uses
+    assert np.allclose(oracle.w_hat(F, 3)[F.mask], F.val.astype(np.float64))
+    assert np.isfinite(y).all()
