@@ -15,7 +15,11 @@ encode()      the reference encoder.  The paper's encoder (section 3.6,
               available, so the activation scale is omitted and every weight
               counts equally (E_c = 1); the pair is the conventional min-max
               lattice of section 3.1 / Appendix D; the pre-grid guard is the
-              ratio criterion of section 3.5.
+              ratio criterion of section 3.5.  Options: the codebook
+              metadata of section 3.1 (pair_fit="codebook") and per-row
+              post-grid picks (post_per_row).  The full encoder, with
+              calibration weights, Lloyd placement and the gain criterion,
+              is in stagq_encoder_full.py.
 codes()       the composite integer u_M of Eq. (8).
 w_main()      the additive reconstruction of Eq. (9) (the direct form; the GPU
               path uses the affine collapse of Eq. (10) instead).
@@ -63,10 +67,12 @@ R9  Codebook metadata: the initial pair (Appendix B) puts the outer two of four
     0.88 / 3 = 0.2933 of the range (the page's "0.29").
 R10 The 256 (lo, s) pairs are s = fp16(2^c_s[i]) and lo = fp16(c_r[j] * s) from
     the fp16 codebook entries, and index i * 16 + j is the stored byte.  Of the
-    page's three placement rules only uniform placement (its fallback) is used.
+    page's three placement rules encode(..., pair_fit="codebook") uses only
+    uniform placement (its fallback); stagq_encoder_full.py has all three.
 R11 In the per-group loss, the pre-grid entry "clipped to the next value
-    inward" is clamped to the range of the group's other entries; E_c = 1 (no
-    calibration data); lambda = 4; the lowest index wins ties.
+    inward" is clamped to the range of the group's other entries; E_c = 1 in
+    encode() (stagq_encoder_full.py takes E_c); lambda = 4; the lowest index
+    wins ties.
 
 Parity status of every function is recorded next to it ("pinned by ...").
 """
