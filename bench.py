@@ -345,29 +345,39 @@ def main():
     dur = {M: [] for M in bits}
 
     if args.mode == "graph":
-        # One graph per precision holding K launches on rotating copies; timing
-        # events sit between the replays on the same stream (ROCm does not allow
-        # timing events inside a captured graph).
+        # The K launches of each precision are split into R equal chunks, one
+        # graph per (precision, chunk) on rotating copies, replayed with the
+        # precisions interleaved (2, 3, 4, 2, 3, 4, ...) so that a slow phase of
+        # the machine does not fall on one precision only.  Timing events sit
+        # between the replays on the same stream (ROCm does not allow timing
+        # events inside a captured graph); each chunk gives one mean per launch.
+        R = next(r for r in (5, 4, 3, 2, 1) if K % r == 0)
+        c = K // R
         graphs = {}
         for M in bits:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in order[M]:
-                    launch(i, M)
-            graphs[M] = g
-            g.replay()
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in order[M][r * c:(r + 1) * c]:
+                        launch(i, M)
+                graphs[M, r] = g
+                g.replay()
         torch.cuda.synchronize()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(bits) + 1)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(R * len(bits) + 1)]
         torch.cuda.synchronize()
         t_start = time.perf_counter()
         evs[0].record()
-        for j, M in enumerate(bits):
-            graphs[M].replay()
-            evs[j + 1].record()
+        n = 0
+        for r in range(R):
+            for M in bits:
+                graphs[M, r].replay()
+                n += 1
+                evs[n].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
         for j, M in enumerate(bits):
-            dur[M] = [evs[j].elapsed_time(evs[j + 1]) * 1e3 / K] * K     # microseconds per launch
+            dur[M] = [evs[r * len(bits) + j].elapsed_time(evs[r * len(bits) + j + 1]) * 1e3 / c
+                      for r in range(R)]                                  # microseconds per launch
     elif args.mode == "stream":
         # The K launches of a precision issued back to back, events around them.
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(bits) + 1)]
