@@ -12,10 +12,11 @@ One step = one GEMV at each precision 2, 3 and 4 bits, each on a different copy
 of the packed image: copies rotate so that consecutive launches never touch
 the same bytes and the working set (>= 700 MB) exceeds the 256 MB Infinity
 Cache, so every launch streams its weights from HBM.  The K timed steps run as
-three captured HIP graphs, one per precision with K launches each (--mode
-graph, default); timing events recorded between the replays on the stream the
-kernels run on give the mean duration of each precision's launches.  --mode
-eager launches from Python with an event pair around every launch instead.
+captured HIP graphs, five chunks of K/5 launches per precision replayed with
+the precisions interleaved (--mode graph, default); timing events recorded
+between the replays on the stream the kernels run on give the mean duration of
+each precision's launches and its spread over the chunks.  --mode eager
+launches from Python with an event pair around every launch instead.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -60,9 +61,11 @@ def read_traffic():
     return out or None
 
 
-def cpu_baseline(rows_sample: int = 1024, target_s: float = 12.0):
+def cpu_baseline(rows_sample: int = 1024, target_s: float = 10.0):
     """The oracle's float64 decode + matvec on the host, on a row sample of the
-    same workload (oracle-encoded), repeated for about target_s seconds."""
+    same workload (oracle-encoded), repeated for about target_s seconds with
+    the host's BLAS threads, then again on one thread (reported in the sample
+    text)."""
     import oracle
     from workloads import WORKLOADS, synth_matrix
     try:
@@ -76,21 +79,34 @@ def cpu_baseline(rows_sample: int = 1024, target_s: float = 12.0):
     G = 4096 // wl.group
     nbytes = {M: rows_sample * 4096 * M // 8 + rows_sample * G * 4 + (rows_sample + 1) * 4 + F.nnz * 8
               + 4096 * 2 + rows_sample * 4 for M in wl.bits}
-    t0 = time.perf_counter()
-    done = 0
-    moved = 0
-    while time.perf_counter() - t0 < target_s or done < 3:
-        for M in wl.bits:
-            oracle.gemv(F, x, M)
-            moved += nbytes[M]
-        done += 1
-    dt = time.perf_counter() - t0
+    round_bytes = sum(nbytes.values())
+
+    def timed(seconds):
+        t0 = time.perf_counter()
+        rounds = []
+        while time.perf_counter() - t0 < seconds or len(rounds) < 3:
+            r0 = time.perf_counter()
+            for M in wl.bits:
+                oracle.gemv(F, x, M)
+            rounds.append(time.perf_counter() - r0)
+        return len(rounds) * round_bytes / sum(rounds) / 1e9, len(rounds), sum(rounds), float(np.median(rounds))
+
+    gbs, done, dt, med = timed(target_s)
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            one = timed(target_s / 2)
+    except Exception:
+        pass
+    one_txt = (f"; on 1 thread {one[0]:.4f} GB/s ({one[1]} rounds, median round {one[3] * 1e3:.1f} ms)"
+               if one else "")
     return {
-        "value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+        "value": round(gbs, 4), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
         "sample": f"{rows_sample}x4096 rows of the same Student-t workload (oracle-encoded), "
-                  f"float64 decode (Eq. 9) + side record + matvec at bits 2,3,4, {done} rounds in {dt:.1f} s; "
-                  f"elementwise NumPy on 1 thread, BLAS matvec on {blas} threads; "
-                  f"host has {os.cpu_count()} logical CPUs",
+                  f"float64 decode (Eq. 9) + side record + matvec at bits 2,3,4, {done} rounds in {dt:.1f} s, "
+                  f"median round {med * 1e3:.1f} ms; elementwise NumPy on 1 thread, BLAS matvec on {blas} "
+                  f"threads{one_txt}; host has {os.cpu_count()} logical CPUs",
     }
 
 
