@@ -1003,7 +1003,9 @@ static size_t lds_layout(int C, int S, bool cb, dev::GemvParams* prm) {
 // 4.65 / 4.97 / 5.04 against 4.81 / 5.19 / 5.45; 5120 x 17920, 573 per block,
 // 11.7 / 13.7 / 14.7 / 19.9 / 21.3 against 11.4 / 15.9 / 15.8 / 20.9 / 22.9
 // (4 bits with depth 1); 4096 x 14336, 229 per block, 7.56 / 7.95 / 8.82
-// against 7.46 / 8.32 / 9.69.
+// against 7.46 / 8.32 / 9.69.  With the record applied after the loop, each
+// wave takes at most 3 steps (4096 x 14336: 7.23 against 7.47 us with 4;
+// 5120 x 17920: 11.20 against 11.43, at 2 bits).
 // STAGQ_WAVES and STAGQ_SIDE override the choices (tuning); STAGQ_FLAG_SPINS
 // sets the side-record wave's spin limit (testing its global-x fallback).
 constexpr int kLightSide = 128;   // side-record entries per block, on average, that the extra wave takes
@@ -1024,6 +1026,7 @@ static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   const int target = 2 * 4 * cus;
   int S = (target + nblk - 1) / nblk;
   if (side && bits <= 4) S = smin;
+  if (!side) S = (Q + 2) / 3;          // after the loop: at most 3 steps per wave
   S = std::max(smin, std::min(smax, S));
   c->prm.flag_spins = env_int("STAGQ_FLAG_SPINS", dev::kFlagSpins);
   const int s_env = env_int("STAGQ_WAVES", 0);

@@ -174,8 +174,8 @@ def test_launch_plan_shapes():
     assert (p5["S"], p5["steps"], p5["threads"]) == (3, 3, 256)
     d = plan(4096, 14336, 2)
     assert (d["grid"], d["S"], d["side"], d["threads"]) == (256, 7, 1, 512)   # no side record: light
-    dh = plan(4096, 14336, 2, nnz=58720)           # 229 entries per block: after the loop
-    assert (dh["S"], dh["side"], dh["threads"]) == (8, 0, 512)
+    dh = plan(4096, 14336, 2, nnz=58720)           # 229 entries per block: after the loop,
+    assert (dh["S"], dh["side"], dh["threads"]) == (10, 0, 640)   # at most 3 steps per wave
     assert plan(4096, 14336, 2, nnz=32768)["side"] == 1 and plan(4096, 14336, 2, nnz=32769)["side"] == 0
     assert plan(4096, 14336, 3, nnz=58720, slots=30)["side"] == 1
     assert plan(4096, 14336, 3, nnz=58720)["side"] == 1                  # heavy, small grid: 2 bits only
