@@ -307,3 +307,23 @@ def test_fixed_slot_side_record_validation():
     with pytest.raises(pwo.StagQError) as e:
         pwo.pack_host(Fb, side_slots=-1)
     assert e.value.status == -4
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU only: --gpus above 1 exits with status 2 and a
+    message, before touching any device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_bench_cpu_baseline_fields():
+    """The CPU baseline is the oracle timed on the host: the contract's fields,
+    a positive rate, the thread count it used, and a sample description."""
+    import bench
+    cb = bench.cpu_baseline(rows_sample=64, target_s=0.5)
+    assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["value"] > 0 and cb["cores"] >= 1
+    assert "64x4096" in cb["sample"]
