@@ -327,3 +327,27 @@ def test_bench_cpu_baseline_fields():
     assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
     assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["value"] > 0 and cb["cores"] >= 1
     assert "64x4096" in cb["sample"]
+
+
+def test_host_code_under_sanitizers(tmp_path):
+    """The library's host encoder, packer and unpacker (no GPU code) run clean
+    under AddressSanitizer and UBSan on a round trip of CSR and fixed-slot
+    images (tests/native/host_roundtrip.cpp, built here with g++)."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("no g++")
+    exe = str(tmp_path / "host_roundtrip")
+    csrc = os.path.join(ROOT, "precision_weight_only_amd", "csrc")
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-pthread", "-I", os.path.join(ROOT, "include"), "-I", csrc,
+           os.path.join(ROOT, "tests", "native", "host_roundtrip.cpp"), os.path.join(csrc, "stagq_host.cpp"),
+           "-o", exe]
+    b = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    if b.returncode != 0 and ("asan" in b.stderr.lower() or "ubsan" in b.stderr.lower()):
+        pytest.skip("sanitizer runtime not available: " + b.stderr[-200:])
+    assert b.returncode == 0, b.stderr[-2000:]
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300,
+                       env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert r.stdout.count("round trip ok") == 6
