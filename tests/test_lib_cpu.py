@@ -331,8 +331,9 @@ def test_bench_cpu_baseline_fields():
 
 def test_host_code_under_sanitizers(tmp_path):
     """The library's host encoder, packer and unpacker (no GPU code) run clean
-    under AddressSanitizer and UBSan on a round trip of CSR and fixed-slot
-    images (tests/native/host_roundtrip.cpp, built here with g++)."""
+    under AddressSanitizer and UBSan on round trips of CSR and fixed-slot
+    images and on malformed fields and images, each rejected with its status
+    (tests/native/host_roundtrip.cpp, built here with g++)."""
     import shutil
     import subprocess
     if shutil.which("g++") is None:
@@ -350,4 +351,4 @@ def test_host_code_under_sanitizers(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300,
                        env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
-    assert r.stdout.count("round trip ok") == 6
+    assert r.stdout.count("round trip ok") == 6 and "all rejected" in r.stdout
