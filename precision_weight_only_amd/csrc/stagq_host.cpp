@@ -138,7 +138,7 @@ uint64_t bytes_read(const ImageHeader& h, int bits) {
 static void pack_rows(const stagq_fields* f, const ImageHeader& h, uint8_t* img, int64_t r0,
                       int64_t r1) {
   const int64_t C = f->cols, n = int64_t(f->rows) * C, T = C / kTileCols;
-  const int N = f->nbits_max, GU = kTileCols / f->group, G = C / f->group;
+  const int N = f->nbits_max, GU = kTileCols / f->group, G = int(C / f->group);
   auto put = [&](uint64_t off, uint32_t v) { memcpy(img + off, &v, 4); };
   for (int64_t r = r0; r < r1; r++)
     for (int64_t t = 0; t < T; t++) {
