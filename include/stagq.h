@@ -45,7 +45,8 @@ extern "C" {
 #define STAGQ_EINVAL  (-1)  /* null pointer, zero size where one is needed, bad argument */
 #define STAGQ_EBITS   (-2)  /* bits outside [2, N] */
 #define STAGQ_ESHAPE  (-3)  /* unsupported rows/cols/group/N, or a stream >= 2 GiB */
-#define STAGQ_ECSR    (-4)  /* malformed side record (row_ptr, col order/range) */
+#define STAGQ_ECSR    (-4)  /* malformed side record (row_ptr, col order/range), or fixed
+                               slots fewer than the fullest row's entries or above 4096 */
 #define STAGQ_EALIGN  (-5)  /* pointer not aligned as documented */
 #define STAGQ_EHIP    (-6)  /* a HIP runtime call failed */
 #define STAGQ_EFIELD  (-7)  /* field out of range: q > 3, plane bit > 1, plane bit set at a
