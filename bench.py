@@ -1,6 +1,8 @@
 """Benchmark of the StagQ batch-one GEMV on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode graph|eager]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--mode graph|stream|eager]
+    python bench.py --sweep          every matrix of every workload
+    python bench.py --read-sweep     plain-read launch shapes at the headline byte counts
 
 Workload: the Llama-3.1-8B gate/up projection, W 14336 x 4096 (rows = output
 channels), Student-t (nu = 4) weights scaled to std 0.02, group 128, base +
@@ -8,16 +10,16 @@ channels), Student-t (nu = 4) weights scaled to std 0.02, group 128, base +
 fp16, batch one.  Weights are synthetic (seeded) and encoded by the library's
 host encoder; nothing is read from disk.
 
-One step = one GEMV at each precision 2, 3 and 4 bits, each on a different copy
-of the packed image: copies rotate so that consecutive launches never touch
-the same bytes and the working set (>= 700 MB) exceeds the 256 MB Infinity
-Cache, so every launch streams its weights from HBM.  The K timed steps run as
-captured HIP graphs, five chunks of K/5 launches per precision replayed with
-the precisions interleaved (--mode graph, default); timing events recorded
-between the replays on the stream the kernels run on give the mean duration of
-each precision's launches and its spread over the chunks.  --mode eager
-launches from Python with an event pair around every launch instead.
-Prints one JSON line.
+The packed image is replicated (63 copies, over 1 GB at 2 bits) so that no
+launch finds its bytes in the 256 MB Infinity Cache: every launch streams its
+weights from HBM.  In graph mode (the default) one HIP graph per precision
+holds one GEMV on every copy, and one step replays the three graphs (2, 3, 4
+bits): 3 x 63 GEMVs.  A spin kernel queued ahead of the timed region keeps
+the GPU busy while the host submits the replays, and timing events between
+the replays, on the stream the kernels run on, give every replay's mean time
+per launch.  --mode stream issues one GEMV per precision per step back to back
+from Python; --mode eager brackets every launch with events.  Prints one JSON
+line.
 """
 from __future__ import annotations
 
@@ -113,22 +115,40 @@ def cpu_baseline(rows_sample: int = 1024, target_s: float = 10.0):
     }
 
 
+def busy_gpu(ms: float = 2.0) -> None:
+    """Queue a spin kernel of about ms milliseconds on the current stream, so the
+    launches queued behind it (while it spins) start back to back instead of
+    waiting for the host to submit them."""
+    import torch
+    try:
+        torch.cuda._sleep(int(ms * 1e6))
+    except Exception:                    # no spin kernel in this build: a few large fills
+        buf = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+        for _ in range(max(1, int(ms * 4))):
+            buf.fill_(1.0)
+
+
 def graph_time(launch, n_copies, K, bits_seq):
-    """Mean microseconds per launch of K launches captured in one HIP graph
-    (launch i uses copy i % n_copies and precision bits_seq[i % len(bits_seq)])."""
+    """Mean microseconds per launch over about K launches: one HIP graph holds
+    n_copies launches (launch i on copy i with precision bits_seq[i % len]),
+    replayed ceil(K / n_copies) times behind a spin kernel, with timing events
+    around the replays on the stream the kernels run on."""
     import torch
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for i in range(K):
-            launch(i % n_copies, bits_seq[i % len(bits_seq)])
+        for i in range(n_copies):
+            launch(i, bits_seq[i % len(bits_seq)])
     g.replay()
     torch.cuda.synchronize()
+    reps = max(1, -(-K // n_copies))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    busy_gpu()
     e0.record()
-    g.replay()
+    for _ in range(reps):
+        g.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / K
+    return e0.elapsed_time(e1) * 1e3 / (reps * n_copies)
 
 
 def codebook_fields(fields):
@@ -179,6 +199,48 @@ def read_ceiling(bytes_alg, args):
                   "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2)}
     del pool
     return out
+
+
+def read_sweep(args):
+    """Plain reads (stagq_stream_read_shape) of the headline GEMV's byte counts at
+    2, 3, 4 bits and of the LM head's at 2 and 4 bits, over threads per
+    workgroup x 16-byte loads per thread in flight x workgroups (0 = one pass,
+    else a persistent grid of that many), each timed like the GEMV: one graph
+    of launches on fresh windows of a 1.5 GB pool, replayed behind a spin
+    kernel.  One JSON line: every shape's microseconds and the best per size."""
+    import torch
+    import precision_weight_only_amd as pwo
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    def alg_bytes(R, C, M, g=128, frac=0.001):   # as stagq_query reports for a CSR image with fp16 pairs
+        nnz = int(np.floor(frac * R * C + 0.5))
+        return R * C * M // 8 + R * (C // g) * 4 + nnz * 8 + (R + 1) * 4 + C * 2 + R * 4
+    sizes = {"gemv_2bit": alg_bytes(14336, 4096, 2), "gemv_3bit": alg_bytes(14336, 4096, 3),
+             "gemv_4bit": alg_bytes(14336, 4096, 4), "lm_head_2bit": alg_bytes(128256, 4096, 2),
+             "lm_head_4bit": alg_bytes(128256, 4096, 4)}
+    pool_bytes = 1536 << 20
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    rows, best = [], {}
+    for name, b in sizes.items():
+        win = (b + 4095) // 4096 * 4096
+        nwin = max(2, min(64, pool_bytes // win))
+        for threads in (256, 512, 1024):
+            for loads in (1, 2, 4, 8, 16):
+                for grid in (0, cus, 2 * cus, 4 * cus, 8 * cus):
+                    def launch(i, _M, b=b, win=win, nwin=nwin, t=threads, l=loads, g=grid):
+                        pwo.stream_read_shape(pool, (i % nwin) * win, b, sink, t, l, g)
+                    us = graph_time(launch, nwin, max(args.steps, 2 * nwin), [0])
+                    one_pass = -(-b // (threads * loads * 16))
+                    r = {"size": name, "bytes": b, "threads": threads, "loads": loads,
+                         "grid": min(grid, one_pass) if grid else one_pass, "persistent": bool(grid and grid < one_pass),
+                         "us": round(us, 3), "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2)}
+                    rows.append(r)
+                    if name not in best or us < best[name]["us"]:
+                        best[name] = r
+        print(f"[read-sweep] {name}: best {best[name]}", file=sys.stderr, flush=True)
+    print(json.dumps({"read_sweep": rows, "best": best, "cus": cus}), flush=True)
 
 
 def sweep(args):
@@ -286,10 +348,69 @@ def sweep(args):
                       "mode": "graph", "data": "synthetic"}), flush=True)
 
 
+HEADLINE = ("mlp", "gate_up")      # the Llama-3.1-8B gate/up projection, 14336 x 4096
+
+
+def make_line(args, mat, wl, dur, bytes_alg, wall, launches_per_step, n_copies, ceiling, plans, nnz,
+              image_bytes):
+    """The JSON line: per-precision timing (dur[M] = microseconds per launch,
+    one value per timed replay or launch), the whole-job rate and the roofline
+    of the dominant launch (the 4-bit GEMV, which moves the most bytes)."""
+    bits = list(wl.bits)
+    K = args.steps
+    per_bits = {}
+    for M in bits:
+        d = np.array(dur[M], dtype=np.float64)
+        mean = float(d.mean())
+        per_bits[str(M)] = {
+            "us_mean": round(mean, 3), "us_median": round(float(np.median(d)), 3),
+            "us_p10": round(float(np.percentile(d, 10)), 3), "us_p90": round(float(np.percentile(d, 90)), 3),
+            "bytes": int(bytes_alg[M]),
+            "gbps": round(bytes_alg[M] / (mean * 1e-6) / 1e9, 1),
+            "pct_peak": round(100.0 * bytes_alg[M] / (mean * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+            "a100_stagq_us": A100_STAGQ_US[M],
+            "read_ceiling": ceiling.get(M),
+            "launch": plans.get(M),
+        }
+    step_bytes = sum(bytes_alg.values()) * launches_per_step
+    value = step_bytes * K / wall / 1e9
+    traffic = read_traffic()
+    dom = max(bits)
+    ach = per_bits[str(dom)]["gbps"]
+    roofline = {
+        "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": round(ach / PEAK_HBM_GBS, 4),
+        "traffic": (traffic or {}).get(dom),
+        "kernel": f"the {dom}-bit GEMV launch (gemv_kernel, M = {dom})",
+        "by_bits": {str(M): {"achieved": per_bits[str(M)]["gbps"],
+                             "frac": round(per_bits[str(M)]["gbps"] / PEAK_HBM_GBS, 4),
+                             "traffic": (traffic or {}).get(M),
+                             "read_ceiling_gbps": (ceiling.get(M) or {}).get("gbps")} for M in bits},
+    }
+    step = (f"one GEMV at each of 2, 3, 4 bits on each of the {n_copies} image copies "
+            f"({3 * launches_per_step} GEMVs), as three HIP graph replays" if launches_per_step > 1 else
+            "one GEMV at each of 2, 3, 4 bits, each on its own image copy")
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"Llama-3.1-8B gate/up GEMV {mat.rows}x{mat.cols}, Student-t(4) std 0.02, "
+                               f"g={wl.group}, base + {wl.nbits - 2} planes, side record {100 * wl.frac:g}%, batch 1",
+                   "rows": mat.rows, "cols": mat.cols, "group": wl.group, "nbits": wl.nbits, "bits": bits,
+                   "side_record_nnz": nnz, "image_bytes": image_bytes,
+                   "rotation_copies": n_copies, "mode": args.mode, "gemvs_per_step": 3 * launches_per_step,
+                   "step": step},
+        "per_bits": per_bits,
+        "roofline": roofline,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--mode", choices=("graph", "stream", "eager"), default="graph",
                     help="graph: K launches per precision captured in one HIP graph; stream: the "
@@ -302,6 +423,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time every matrix of every workload instead of the headline line")
+    ap.add_argument("--read-sweep", action="store_true",
+                    help="time plain reads of the headline byte counts and of the LM head's over a "
+                         "grid of launch shapes (threads, loads in flight, workgroups)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run 5 device-to-device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -318,17 +442,20 @@ def main():
     if args.sweep:
         sweep(args)
         return
+    if args.read_sweep:
+        read_sweep(args)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = WORKLOADS["mlp"]
-    mat = wl.matrices[0]                       # gate/up 14336 x 4096
+    wl = WORKLOADS[HEADLINE[0]]
+    mat = [m for m in wl.matrices if m.name == HEADLINE[1]][0]
     R, Cc = mat.rows, mat.cols
     bits = list(wl.bits)
 
     t0 = time.time()
     w, x = synth_matrix(R, Cc, wl.dist, mat.seed)
-    K = int(np.floor(wl.frac * R * Cc + 0.5))
-    fields = pwo.encode(w, wl.group, wl.nbits, K, wl.ratio_T)
+    side_budget = int(np.floor(wl.frac * R * Cc + 0.5))
+    fields = pwo.encode(w, wl.group, wl.nbits, side_budget, wl.ratio_T)
     base = pwo.StagQMatrix.pack(fields, device=dev)
     # Enough copies that the lowest precision's reads of all of them exceed
     # the rotation size, and every precision cycles through all of them.
@@ -362,41 +489,46 @@ def main():
     # launch ids per precision: each precision cycles through every copy
     order = {M: [j * K + s for s in range(K)] for j, M in enumerate(bits)}
     dur = {M: [] for M in bits}
+    launches_per_step = 1          # GEMVs per precision in one step
 
     if args.mode == "graph":
-        # The K launches of each precision are split into R equal chunks, one
-        # graph per (precision, chunk) on rotating copies, replayed with the
-        # precisions interleaved (2, 3, 4, 2, 3, 4, ...) so that a slow phase of
-        # the machine does not fall on one precision only.  Timing events sit
-        # between the replays on the same stream (ROCm does not allow timing
-        # events inside a captured graph); each chunk gives one mean per launch.
-        R = next(r for r in (5, 4, 3, 2, 1) if K % r == 0)
-        c = K // R
+        # One HIP graph per precision holds one launch on every image copy
+        # (n_copies launches); a step replays the three graphs, precisions
+        # interleaved (2, 3, 4), so a step is n_copies GEMVs at each precision
+        # and every graph is as long whatever K is.  A spin kernel ahead of the
+        # first timing event keeps the GPU busy while the host submits the
+        # replays, so no launch waits for the host; timing events between the
+        # replays, on the stream the kernels run on, give each replay's mean
+        # microseconds per launch.
         graphs = {}
         for M in bits:
-            for r in range(R):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    for i in order[M][r * c:(r + 1) * c]:
-                        launch(i, M)
-                graphs[M, r] = g
-                g.replay()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in range(n_copies):
+                    launch(c, M)
+            graphs[M] = g
+            g.replay()
         torch.cuda.synchronize()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(R * len(bits) + 1)]
+        for _ in range(args.warmup):
+            for M in bits:
+                graphs[M].replay()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(K * len(bits) + 1)]
         torch.cuda.synchronize()
+        busy_gpu()
         t_start = time.perf_counter()
         evs[0].record()
         n = 0
-        for r in range(R):
+        for s in range(K):
             for M in bits:
-                graphs[M, r].replay()
+                graphs[M].replay()
                 n += 1
                 evs[n].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
         for j, M in enumerate(bits):
-            dur[M] = [evs[r * len(bits) + j].elapsed_time(evs[r * len(bits) + j + 1]) * 1e3 / c
-                      for r in range(R)]                                  # microseconds per launch
+            dur[M] = [evs[s * len(bits) + j].elapsed_time(evs[s * len(bits) + j + 1]) * 1e3 / n_copies
+                      for s in range(K)]                                  # microseconds per launch
+        launches_per_step = n_copies
     elif args.mode == "stream":
         # The K launches of a precision issued back to back, events around them.
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(bits) + 1)]
@@ -430,52 +562,9 @@ def main():
 
     bytes_alg = {M: base.bytes_read[M] for M in bits}
     ceiling = read_ceiling(bytes_alg, args) if args.mode == "graph" else {}
-    per_bits = {}
-    for M in bits:
-        d = np.array(dur[M])
-        mean = float(d.mean())
-        per_bits[str(M)] = {
-            "us_mean": round(mean, 3), "us_median": round(float(np.median(d)), 3),
-            "us_p10": round(float(np.percentile(d, 10)), 3), "us_p90": round(float(np.percentile(d, 90)), 3),
-            "bytes": int(bytes_alg[M]),
-            "gbps": round(bytes_alg[M] / (mean * 1e-6) / 1e9, 1),
-            "pct_peak": round(100.0 * bytes_alg[M] / (mean * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
-            "a100_stagq_us": A100_STAGQ_US[M],
-            "read_ceiling": ceiling.get(M),
-            "launch": base.plan(M),
-        }
-    step_bytes = sum(bytes_alg.values())
-    value = step_bytes * K / wall / 1e9
-
-    traffic = read_traffic()
-    dom = 4                                        # the 4-bit read moves the most bytes per step
-    ach = per_bits[str(dom)]["gbps"]
-    roofline = {
-        "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-        "frac": round(ach / PEAK_HBM_GBS, 4),
-        "traffic": (traffic or {}).get(dom),
-        "kernel": f"gemv_kernel<M={dom}> (bits={dom})",
-        "by_bits": {str(M): {"achieved": per_bits[str(M)]["gbps"],
-                             "frac": round(per_bits[str(M)]["gbps"] / PEAK_HBM_GBS, 4),
-                             "traffic": (traffic or {}).get(M),
-                             "read_ceiling_gbps": (ceiling.get(M) or {}).get("gbps")} for M in bits},
-    }
-    out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "Llama-3.1-8B gate/up GEMV 14336x4096, Student-t(4) std 0.02, g=128, "
-                               "base + 2 planes, side record 0.1%, batch 1",
-                   "rows": R, "cols": Cc, "group": wl.group, "nbits": wl.nbits, "bits": bits,
-                   "side_record_nnz": int(base.nnz), "image_bytes": int(base.image_bytes),
-                   "rotation_copies": n_copies, "mode": args.mode,
-                   "step": "one GEMV at each of 2, 3, 4 bits, each on its own image copy"},
-        "per_bits": per_bits,
-        "roofline": roofline,
-        "setup_s": round(setup_s, 2),
-        "kernel_source_sha256_16": kernel_source_hash(),
-    }
+    out = make_line(args, mat, wl, dur, bytes_alg, wall, launches_per_step, n_copies, ceiling,
+                    {M: base.plan(M) for M in bits}, int(base.nnz), int(base.image_bytes))
+    out["setup_s"] = round(setup_s, 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
