@@ -223,7 +223,8 @@ int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, in
 
 /*
  * Streaming-read ceiling (measurement aid, not part of the method): read bytes
- * of device memory at buf once, 16-byte loads, 16 KB per 256-thread
+ * of device memory at buf once, 16-byte loads with the non-temporal cache
+ * policy the GEMV uses for its weight stream, 16 KB per 256-thread
  * workgroup, and discard them (sink, device uint32 [1], is written only when
  * a checksum of the data hits one 32-bit value, which keeps the loads alive).  Timing this on
  * the byte count a GEMV moves gives the plain-read time of those bytes on this
@@ -233,6 +234,23 @@ int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, in
  * error.
  */
 int stagq_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* hip_stream);
+
+/*
+ * Streaming read of a chosen launch shape (measurement aid for the read-ceiling
+ * sweep, not part of the method): grid workgroups of threads threads each
+ * (a multiple of 64 in [64, 1024]); in every pass a thread issues loads
+ * (1, 2, 4, 8 or 16) 16-byte non-temporal loads before it uses them, every wave instruction
+ * one contiguous 1 KB piece, and the grid strides over buf until all bytes
+ * have been read once.  grid == 0 launches as many workgroups as one pass
+ * needs (ceil(bytes / (threads * loads * 16))); a smaller grid makes a
+ * persistent read of several passes.  Data are discarded as in
+ * stagq_stream_read (sink written only on one checksum value).  buf 16-byte
+ * aligned, bytes < 2^31; bytes == 0 does nothing.  STAGQ_EINVAL for NULL
+ * pointers, a byte count >= 2^31 or a shape outside these sets, STAGQ_EALIGN,
+ * STAGQ_EHIP on a launch error.
+ */
+int stagq_stream_read_shape(const void* buf, size_t bytes, uint32_t* sink, int threads, int loads,
+                            int grid, void* hip_stream);
 
 /* Fill *out with shape and per-precision traffic of h. */
 int stagq_query(stagq_handle h, stagq_info* out);

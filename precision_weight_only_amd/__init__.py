@@ -87,6 +87,41 @@ def stream_read(buf, offset: int, nbytes: int, sink, stream=None) -> None:
                                   C.c_void_p(sink.data_ptr()), _stream_ptr(stream)), "stagq_stream_read")
 
 
+def stream_read_shape(buf, offset: int, nbytes: int, sink, threads: int, loads: int, grid: int = 0,
+                      stream=None) -> None:
+    """Plain read of nbytes of buf from offset with a chosen launch shape
+    (threads per workgroup, 16-byte loads per thread per pass, workgroups;
+    grid 0 = one pass): the read-ceiling sweep."""
+    if offset % 16 or offset + nbytes > buf.numel():
+        raise ValueError("stream_read_shape: offset must be a multiple of 16 and the window inside buf")
+    check(lib().stagq_stream_read_shape(C.c_void_p(buf.data_ptr() + offset), int(nbytes),
+                                        C.c_void_p(sink.data_ptr()), int(threads), int(loads), int(grid),
+                                        _stream_ptr(stream)), "stagq_stream_read_shape")
+
+
+def check_gemv_args(rows: int, cols: int, device, x, y, x_scale=None) -> None:
+    """Raise ValueError (TypeError for non-tensors) unless x is a contiguous fp16
+    vector of cols elements, x_scale (if given) likewise, and y a contiguous
+    fp32 or fp16 vector of at least rows elements, all on device.  Runs before
+    any launch: the library checks only pointers and alignment."""
+    torch = _torch()
+    for name, t, dtypes, n, exact in (("x", x, (torch.float16,), cols, True),
+                                      ("x_scale", x_scale, (torch.float16,), cols, True),
+                                      ("y", y, (torch.float32, torch.float16), rows, False)):
+        if t is None and name == "x_scale":
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"gemv: {name} must be a torch tensor")
+        if t.dtype not in dtypes:
+            raise ValueError(f"gemv: {name} must be {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+        if (t.numel() != n) if exact else (t.numel() < n):
+            raise ValueError(f"gemv: {name} has {t.numel()} elements, needs {'exactly' if exact else 'at least'} {n}")
+        if not t.is_contiguous():
+            raise ValueError(f"gemv: {name} must be contiguous")
+        if t.device != device:
+            raise ValueError(f"gemv: {name} is on {t.device}, the image on {device}")
+
+
 def _size_error(fs) -> None:
     """stagq_packed_bytes gave 0: raise the status validation reports (the
     packer validates before it looks at its destination)."""
@@ -194,14 +229,13 @@ class StagQMatrix:
         to x as it is staged (stagq_gemv_scaled)."""
         torch = _torch()
         if y is None:
-            y = torch.empty(self.rows, dtype=out_dtype or torch.float32, device=x.device)
+            y = torch.empty(self.rows, dtype=out_dtype or torch.float32, device=self.buffer.device)
+        check_gemv_args(self.rows, self.cols, self.buffer.device, x, y, x_scale)
         if y.dtype == torch.float16:
             check(lib().stagq_gemv_f16(self._h, C.c_void_p(x.data_ptr()),
                                        C.c_void_p(x_scale.data_ptr()) if x_scale is not None else None,
                                        C.c_void_p(y.data_ptr()), int(bits), _stream_ptr(stream)),
                   "stagq_gemv_f16")
-        elif y.dtype != torch.float32:
-            raise TypeError("gemv: y must be float32 or float16")
         elif x_scale is None:
             check(lib().stagq_gemv(self._h, C.c_void_p(x.data_ptr()), C.c_void_p(y.data_ptr()),
                                    int(bits), _stream_ptr(stream)), "stagq_gemv")
@@ -219,6 +253,10 @@ class StagQMatrix:
         torch = _torch()
         if out is None:
             out = torch.empty((self.rows, self.cols), dtype=torch.uint8, device=self.buffer.device)
+        if out.dtype != torch.uint8 or out.numel() < self.rows * self.cols or not out.is_contiguous() \
+                or out.device != self.buffer.device:
+            raise ValueError("decode_codes: out must be a contiguous uint8 tensor of at least rows * cols "
+                             "elements on the image's device")
         check(lib().stagq_decode_codes(self._h, int(bits), C.c_void_p(out.data_ptr()),
                                        _stream_ptr(stream)), "stagq_decode_codes")
         return out

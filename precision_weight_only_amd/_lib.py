@@ -72,6 +72,7 @@ def _load() -> C.CDLL:
         "stagq_plan_gemv": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int64, C.c_int32,
                                       C.c_int, P]),
         "stagq_stream_read": (C.c_int, [P, C.c_size_t, P, P]),
+        "stagq_stream_read_shape": (C.c_int, [P, C.c_size_t, P, C.c_int, C.c_int, C.c_int, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -87,7 +88,7 @@ EXPORTED = (
     "stagq_packed_bytes", "stagq_pack_host", "stagq_pack", "stagq_rebind", "stagq_gemv",
     "stagq_decode_codes", "stagq_query", "stagq_destroy", "stagq_strerror", "stagq_encode",
     "stagq_unpack_host", "stagq_plan_gemv", "stagq_stream_read", "stagq_gemv_scaled",
-    "stagq_gemv_f16",
+    "stagq_gemv_f16", "stagq_stream_read_shape",
 )
 
 

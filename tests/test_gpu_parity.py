@@ -255,14 +255,22 @@ def test_error_codes(pwo):
         assert e.value.status == -2
     xbig = torch.zeros(F.cols + 8, dtype=torch.float16, device="cuda")
     with pytest.raises(pwo.StagQError) as e:
-        m.gemv(xbig[1:], 3)                      # 2-byte offset: not 16-byte aligned
+        m.gemv(xbig[1:F.cols + 1], 3)            # 2-byte offset: not 16-byte aligned
     assert e.value.status == -5
     with pytest.raises(pwo.StagQError) as e:
         m.decode_codes(7)
     assert e.value.status == -2
     with pytest.raises(pwo.StagQError) as e:
-        m.gemv(xd, 3, x_scale=xbig[1:])          # misaligned scale
+        m.gemv(xd, 3, x_scale=xbig[1:F.cols + 1])   # misaligned scale
     assert e.value.status == -5
+    # the binding's own checks, before any launch
+    for bad in (xbig, xd.float(), xd.cpu(), torch.zeros(2 * F.cols, dtype=torch.float16, device="cuda")[::2]):
+        with pytest.raises(ValueError):
+            m.gemv(bad, 3)
+    with pytest.raises(ValueError):
+        m.gemv(xd, 3, y=torch.empty(F.rows - 1, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        m.gemv(xd, 3, y=torch.empty(F.rows, dtype=torch.float64, device="cuda"))
     assert pwo.lib().stagq_gemv_scaled(m._h, xd.data_ptr(), None, xd.data_ptr(), 3, None) == -1
 
 

@@ -352,3 +352,103 @@ def test_host_code_under_sanitizers(tmp_path):
                        env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
     assert r.stdout.count("round trip ok") == 6 and "all rejected" in r.stdout
+
+
+def test_gemv_argument_checks_before_launch():
+    """The binding rejects a wrong dtype, length, layout or device of x, x_scale
+    or y with ValueError before it calls the library (meta tensors: nothing
+    here can reach a device)."""
+    import torch
+    dev = torch.device("meta")
+    R, Cc = 48, 256
+    x = torch.empty(Cc, dtype=torch.float16, device=dev)
+    y = torch.empty(R, dtype=torch.float32, device=dev)
+    pwo.check_gemv_args(R, Cc, dev, x, y)                                   # valid: no error
+    pwo.check_gemv_args(R, Cc, dev, x, torch.empty(R + 3, dtype=torch.float16, device=dev), x)
+    bad = [
+        (torch.empty(Cc, dtype=torch.float32, device=dev), y, None),       # x not fp16
+        (torch.empty(Cc + 8, dtype=torch.float16, device=dev), y, None),   # x too long
+        (torch.empty(Cc - 8, dtype=torch.float16, device=dev), y, None),   # x too short
+        (torch.empty(2 * Cc, dtype=torch.float16, device=dev)[::2], y, None),  # x strided
+        (torch.empty(Cc, dtype=torch.float16), y, None),                    # x on another device
+        (x, torch.empty(R - 1, dtype=torch.float32, device=dev), None),     # y too short
+        (x, torch.empty(R, dtype=torch.float64, device=dev), None),         # y not fp32 / fp16
+        (x, torch.empty(2 * R, dtype=torch.float32, device=dev)[::2], None),  # y strided
+        (x, y, torch.empty(Cc - 8, dtype=torch.float16, device=dev)),       # scale too short
+        (x, y, torch.empty(Cc, dtype=torch.float32, device=dev)),           # scale not fp16
+    ]
+    for xx, yy, ss in bad:
+        with pytest.raises(ValueError):
+            pwo.check_gemv_args(R, Cc, dev, xx, yy, ss)
+    with pytest.raises(TypeError):
+        pwo.check_gemv_args(R, Cc, dev, np.zeros(Cc, np.float16), y)
+
+
+def test_launch_plan_every_width_and_precision():
+    """Every shape the packer accepts has a launch plan (cols up to 32768 in
+    steps of 128, every group size, N = 8 at every precision, with and without
+    a heavy side record): the widest rows apply the side record after the loop
+    when the extra wave does not fit."""
+    out = (C.c_int32 * 8)()
+    for Cc in list(range(128, 32769, 128)):
+        for g in (32, 64, 128):
+            for bits in (2, 3, 4, 8):
+                for nnz in (0, 200 * 64):
+                    st = pwo.lib().stagq_plan_gemv(64, Cc, g, 8, nnz, 0, bits, out)
+                    assert st == 0, (Cc, g, bits, nnz, st)
+                    assert 0 < out[1] <= 1024 and out[5] <= 160 * 1024
+    assert pwo.lib().stagq_plan_gemv(64, 32768, 128, 4, 0, 0, 2, out) == 0 and out[6] == 0
+
+
+def test_stream_read_shape_argument_errors():
+    lib = pwo.lib()
+    sink = C.c_void_p(64)
+    buf = C.c_void_p(4096)
+    assert lib.stagq_stream_read_shape(None, 4096, sink, 256, 1, 0, None) == -1
+    assert lib.stagq_stream_read_shape(buf, 4096, None, 256, 1, 0, None) == -1
+    assert lib.stagq_stream_read_shape(buf, 1 << 31, sink, 256, 1, 0, None) == -1
+    for threads, loads, grid in ((32, 1, 0), (1088, 1, 0), (100, 1, 0), (256, 3, 0), (256, 32, 0), (256, 1, -1)):
+        assert lib.stagq_stream_read_shape(buf, 4096, sink, threads, loads, grid, None) == -1
+    assert lib.stagq_stream_read_shape(C.c_void_p(4104), 4096, sink, 256, 1, 0, None) == -5
+    assert lib.stagq_stream_read_shape(buf, 0, sink, 256, 1, 0, None) == 0
+
+
+def test_bench_line_names_the_headline_shape():
+    """The JSON line reports the shape it timed (14336 x 4096) and a roofline
+    fraction that is the 4-bit GEMV's algorithmic bytes over its mean time."""
+    import types
+    import bench
+    from workloads import WORKLOADS
+    wl = WORKLOADS[bench.HEADLINE[0]]
+    mat = [m for m in wl.matrices if m.name == bench.HEADLINE[1]][0]
+    args = types.SimpleNamespace(steps=20, warmup=5, mode="graph")
+    bytes_alg = {2: 17107716, 3: 24447748, 4: 31787780}
+    dur = {2: [6.0] * 20, 3: [7.0] * 20, 4: [8.0] * 20}
+    line = bench.make_line(args, mat, wl, dur, bytes_alg, wall=0.03, launches_per_step=63, n_copies=63,
+                           ceiling={}, plans={}, nnz=58720, image_bytes=31840256)
+    assert (line["config"]["rows"], line["config"]["cols"]) == (14336, 4096)
+    assert line["config"]["gemvs_per_step"] == 189
+    assert line["roofline"]["achieved"] == round(31787780 / 8.0e-6 / 1e9, 1)
+    assert abs(line["roofline"]["frac"] - 31787780 / 8.0e-6 / 1e9 / 8000) < 1e-4
+    assert line["value"] == round(sum(bytes_alg.values()) * 63 * 20 / 0.03 / 1e9, 1)
+
+
+def test_bench_codebook_fields_select_the_oracle_pairs():
+    """bench.codebook_fields (the full-size codebook timing workload) builds
+    indices whose (lo, s) are exactly the pairs the oracle's codebook table
+    (reading R10) gives for those indices, and the packer accepts them."""
+    import bench
+    import oracle
+    from workloads import synth_matrix
+    w, _ = synth_matrix(96, 512, "student_t", 3)
+    F = oracle.encode(w, 128, 4, 0.01)
+    d = dict(q=F.q, planes=F.planes, lo=F.lo, s=F.s, row_ptr=F.row_ptr, col=F.col, val=F.val,
+             group=F.group, nbits=F.nbits)
+    cb = bench.codebook_fields(d)
+    tlo, ts = oracle.codebook_table(cb["cb_log2s"], cb["cb_ratio"])
+    assert np.array_equal(tlo[cb["idx"]].view(np.uint16), np.asarray(cb["lo"], np.float16).view(np.uint16))
+    assert np.array_equal(ts[cb["idx"]].view(np.uint16), np.asarray(cb["s"], np.float16).view(np.uint16))
+    img = pwo.pack_host(cb)
+    back = pwo.unpack_host(img)
+    assert back["codebook"] == 1
+    assert np.array_equal(back["lo"].view(np.uint16), np.asarray(cb["lo"], np.float16).view(np.uint16))
