@@ -469,3 +469,55 @@ def test_per_row_post_grid_pick_by_brute_force():
         res.sort(key=lambda t: (-t[0], t[1]))
         want = {c for _, c in res[:k]} | {f - r * 256 for f in pre if f // 256 == r}
         assert set(np.nonzero(F.mask[r])[0].tolist()) == want, r
+
+
+# ------------------------------------------------------- budget and row blocks
+def test_budget_rounds_halves_up_hand_worked():
+    """K = round(frac R C) with a half rounded up (the reading the oracle takes
+    where the pages give only a fraction): worked by hand on products that are
+    exactly k + 1/2 in binary, and on ones that are not."""
+    assert oracle.budget(0.25, 2, 5) == 3        # 2.5 -> 3
+    assert oracle.budget(0.5, 1, 7) == 4         # 3.5 -> 4
+    assert oracle.budget(0.375, 1, 4) == 2       # 1.5 -> 2
+    assert oracle.budget(0.125, 4, 1) == 1       # 0.5 -> 1
+    assert oracle.budget(0.25, 1, 9) == 2        # 2.25 -> 2
+    assert oracle.budget(0.25, 1, 11) == 3       # 2.75 -> 3
+    assert oracle.budget(0.0, 64, 64) == 0
+    # the encoder holds out exactly that many on a matrix whose budget is a tie
+    w = np.array([[0.0, 0.1, 0.2, 0.3, 9.0],
+                  [0.5, -0.4, 0.1, 0.05, 0.0]], np.float16)
+    F = oracle.encode(w, 5, 4, 0.25)              # 0.25 * 2 * 5 = 2.5 -> 3 entries
+    assert F.nnz == 3
+    # by hand: the 9.0 is 30x the next largest of its group (pre-grid, T = 4);
+    # the remaining two are the largest two-bit residuals of the rest
+    assert F.mask[0, 4] and F.n_pre == 1 and F.n_post == 2
+
+
+def test_row_blocks_past_the_first_against_exact_rationals():
+    """gemv() with row blocks smaller than the matrix (blocks starting past row
+    0) and w_hat() on a row slice equal the exact-rational reconstruction of
+    Eq. 4 with Eq. 10, entry by entry, including rows with side-record entries."""
+    w, x = synth_matrix(7, 64, "normal_outliers", 33)
+    F = oracle.encode(w, 32, 4, 0.05)
+    assert F.nnz > 0 and len(set(np.nonzero(F.mask)[0])) >= 3
+    xs = [Fraction(float(v)) for v in x]
+    for M in range(2, 5):
+        u = oracle.codes(F, M)
+
+        def exact(r, c):
+            j = c // F.group
+            lo, s = Fraction(float(F.lo[r, j])), Fraction(float(F.s[r, j]))
+            main = lo - s * (2 ** (M - 2) - 1) / Fraction(2) ** (M - 1) + s / Fraction(2) ** (M - 2) * int(u[r, c])
+            return Fraction(float(w[r, c])) if F.mask[r, c] else main
+
+        for block_rows in (1, 2, 3):
+            y = oracle.gemv(F, x, M, block_rows=block_rows)
+            for r in range(F.rows):
+                yr = sum(exact(r, c) * xs[c] for c in range(F.cols))
+                assert abs(float(yr) - y[r]) <= 1e-12 * max(1.0, abs(float(yr)))
+        for r0, r1 in ((2, 5), (6, 7), (1, 7)):
+            wh = oracle.w_hat(F, M, slice(r0, r1))
+            assert wh.shape == (r1 - r0, F.cols)
+            for r in range(r0, r1):
+                for c in range(F.cols):
+                    assert wh[r - r0, c] == float(exact(r, c))
