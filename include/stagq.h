@@ -199,8 +199,10 @@ int stagq_gemv_f16(stagq_handle h, const void* x, const void* x_scale, void* y, 
                    void* hip_stream);
 
 /*
- * Write the composite integers u_bits (Eq. 8) of the main stream as decoded by
- * the GEMV path: codes is device uint8 [rows*cols], row-major, 16-byte aligned.
+ * Write the composite integers u_bits (Eq. 8) of the main stream, read field
+ * by field from the packed image by a kernel of its own (the GEMV decodes
+ * them with different arithmetic; its decode is checked through y):
+ * codes is device uint8 [rows*cols], row-major, 16-byte aligned.
  * Asynchronous on hip_stream.  (Held-out positions decode like any other: q
  * followed by zero planes.)
  */
@@ -215,8 +217,10 @@ int stagq_decode_codes(stagq_handle h, int bits, uint8_t* codes, void* hip_strea
  * out[2] waves per workgroup that stream the main stream, out[3] steps per
  * such wave (a step is 16 rows x 4 tile columns of 128), out[4] rows per
  * workgroup, out[5] LDS bytes, out[6] 1 if the side record runs on an extra
- * wave of each workgroup (else 0), out[7] steps of loads in flight per wave.
- * out is host int32[8].  Pure host logic.
+ * wave of each workgroup (else 0), out[7] steps of loads in flight per wave,
+ * out[8] 1 if a wave requests its next step as soon as the current one has
+ * arrived (early issue; else once it is decoded).  out is host int32[9].
+ * Pure host logic.
  */
 int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, int64_t nnz,
                     int32_t side_slots, int bits, int32_t* out);

@@ -69,11 +69,11 @@ def encode(w16: np.ndarray, group: int, nbits: int, budget: int, ratio_T: float 
 def plan_gemv(rows: int, cols: int, group: int, nbits: int, bits: int, nnz: int = 0,
               side_slots: int = 0) -> Dict[str, int]:
     """Launch shape the library picks for this GEMV (workgroups, threads, ...)."""
-    out = (C.c_int32 * 8)()
+    out = (C.c_int32 * 9)()
     check(lib().stagq_plan_gemv(rows, cols, group, nbits, int(nnz), int(side_slots), bits,
                                 C.cast(out, C.c_void_p)), "stagq_plan_gemv")
     keys = ("grid", "threads", "waves", "steps_per_wave", "rows_per_group", "lds_bytes",
-            "side_wave", "depth")
+            "side_wave", "depth", "early_issue")
     return dict(zip(keys, list(out)))
 
 

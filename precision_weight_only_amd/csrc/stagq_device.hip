@@ -211,6 +211,17 @@ __device__ __forceinline__ void issue(Slot<M, GU>& s, const rsrc_t& rU, uint32_t
     s.pl[k] = __builtin_amdgcn_raw_buffer_load_b128(rU, off, so + (k + 2) * 1024, kStream);
 }
 
+// An empty statement that reads every register of a slot: the wave waits here
+// until all of the slot's loads have arrived (and nothing is computed).
+template <int M, int GU>
+__device__ __forceinline__ void touch(const Slot<M, GU>& s) {
+  asm volatile("" :: "v"(s.a), "v"(s.b));
+#pragma unroll
+  for (int g = 0; g < GU; g++) asm volatile("" :: "v"(s.meta[g]));
+#pragma unroll
+  for (int k = 0; k < M - 2; k++) asm volatile("" :: "v"(s.pl[k]));
+}
+
 __device__ __forceinline__ uint32_t s0_dword(const u32x4& a, const u32x4& b, int dw) {
   return dw < 4 ? a[dw] : b[dw - 4];
 }
@@ -576,7 +587,7 @@ __device__ __forceinline__ void side_slots_wave(const GemvParams& p, int blk, in
 // p.xsc as it is staged (each product rounded once to fp16).  CB: the group
 // metadata is a codebook index per group; each wave keeps its own LDS copy of
 // the 256 pairs (1 KB) and looks the pair up once per group.
-template <int M, int GU, int D, int SIDE, bool SC, bool CB>
+template <int M, int GU, int D, int SIDE, bool SC, bool CB, bool E>
 __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
   uint32_t* xs = reinterpret_cast<uint32_t*>(lds);            // x pairs, tile t at t * kXPitch
@@ -654,7 +665,7 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  Slot<M, GU> sl[D];
+  Slot<M, GU> sl[E ? D + 1 : D];
   u32x4 tabv;
   if constexpr (CB) tabv = ld128(mk(p.table, 1024u), 16u * uint32_t(lane));
   issue<M, GU, CB>(sl[0], rU, uo0, vW, vM, valid(0));
@@ -754,17 +765,36 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   // LDS x of the lane's tile at step i: tile 4 (q0 + i) + cg (zero x past
   // the row's end, where the weights are zero tiles too).
   const int xo0 = (4 * q0 + cg) * kXPitch;
-  auto step = [&](Slot<M, GU>& s, int i) {
-    if (i < nq) part = tile_partial<M, GU, CB>(s, xs + xo0 + 4 * kXPitch * i, part, tab_s);
-    __builtin_amdgcn_sched_barrier(0);   // reuse the slot's registers: no loads hoisted above
-    issue<M, GU, CB>(s, rU, uo0 + uint32_t(i + D) * p.unit_bytes, vW, vM, valid(i + D));
-  };
+  if constexpr (E) {
+    // Early issue: D steps in flight and one more slot being decoded; step
+    // i + D is requested as soon as step i has arrived, before step i is
+    // decoded (a wave takes at most kXChunks steps, so the loop unrolls fully).
 #pragma unroll
-  for (int i = 0; i < D; i++) step(sl[i], i);
-  __builtin_amdgcn_s_setprio(0);                  // the remaining steps
-  for (int ib = D; ib < nq; ib += D) {
+    for (int i = 0; i < kXChunks; i++) {
+      if (i == D) __builtin_amdgcn_s_setprio(0);
+      Slot<M, GU>& cur = sl[i % (D + 1)];
+      touch(cur);
+      __builtin_amdgcn_sched_barrier(0);
+      issue<M, GU, CB>(sl[(i + D) % (D + 1)], rU, uo0 + uint32_t(i + D) * p.unit_bytes, vW, vM, valid(i + D));
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < nq) part = tile_partial<M, GU, CB>(cur, xs + xo0 + 4 * kXPitch * i, part, tab_s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // D steps in flight; the slot of step i is reloaded with step i + D once
+    // step i is decoded.
+    auto step = [&](Slot<M, GU>& s, int i) {
+      if (i < nq) part = tile_partial<M, GU, CB>(s, xs + xo0 + 4 * kXPitch * i, part, tab_s);
+      __builtin_amdgcn_sched_barrier(0);   // reuse the slot's registers: no loads hoisted above
+      issue<M, GU, CB>(s, rU, uo0 + uint32_t(i + D) * p.unit_bytes, vW, vM, valid(i + D));
+    };
 #pragma unroll
-    for (int i = 0; i < D; i++) step(sl[i], ib + i);
+    for (int i = 0; i < D; i++) step(sl[i], i);
+    __builtin_amdgcn_s_setprio(0);                  // the remaining steps
+    for (int ib = D; ib < nq; ib += D) {
+#pragma unroll
+      for (int i = 0; i < D; i++) step(sl[i], ib + i);
+    }
   }
 
   part_s[w * 64 + lane] = part;
@@ -954,7 +984,8 @@ __global__ void __launch_bounds__(256) codes_kernel(const CodesParams p) {
 struct LaunchCfg {
   int S, grid, nt_max;
   bool side;                    // side record on an extra wave (SIDE mode)
-  bool deep;                    // the deeper depth table (see kDepthMany)
+  int depth;                    // steps of loads in flight per wave (1 or 2)
+  bool early;                   // early issue (step i + depth requested when step i arrives)
   size_t lds;
   dev::GemvParams prm;
 };
@@ -986,18 +1017,36 @@ static int env_int(const char* name, int dflt) {
   return e ? atoi(e) : dflt;
 }
 
-// Steps of loads in flight per wave, per precision: with the side-record wave
-// on grids of two or more workgroups per CU or with a light (or fixed-slot)
-// record, and otherwise (a heavy record on a smaller grid, or the record
-// applied after the loop).  Shallow on purpose: with two to four waves per SIMD
-// the chip holds enough bytes in flight, and deeper per-wave queues only delay
-// every wave's first data.  Measured: depth 2 beats 3 and 4 at 2-3 bits
-// (14336 x 4096, 4096 x 14336); at 4 bits depth 2 beats 1 on 17920 x 5120
-// (12.5 against 13.4 us), 14336 x 4096 (8.5 against 8.8) and 4096 x 4096 with
-// a light record (5.05 against 6.44) but loses on 5120 x 17920 with a heavy one
-// (16.9 against 14.7 us); from 5 bits depth 1 wins.
-constexpr int kDepthMany[9] = {0, 0, 2, 2, 2, 1, 1, 1, 1};
-constexpr int kDepthFew[9] = {0, 0, 2, 2, 1, 1, 1, 1, 1};
+// Loads in flight per wave ("depth") and the issue mode.  A wave requests its
+// first D steps before it computes; then either (plain) the slot of step i is
+// reloaded with step i + D once step i is decoded, or (early issue) step i + D
+// goes out as soon as step i has arrived, into a spare slot, so the request
+// overlaps the decode of step i.  On this GPU requests issued together come
+// back together (with every step of a wave in flight, its first step arrives
+// near the end of the whole transfer, measured per wave with s_memrealtime), so
+// a shallow depth that re-issues on arrival keeps the data flowing while the
+// decode follows it.  Measured in one session (us at 2 / 3 / 4 bits, the
+// weight stream loaded non-temporal):
+//   14336 x 4096 (3.5 blocks per CU, light record): early depth 1 5.82 / 6.63 /
+//     7.69; plain depth 2 5.89 / 6.78 / 7.94; plain depth 1 7.08 / 7.88 / 8.19
+//   17920 x 5120 (4.4 blocks per CU): early depth 1 8.57 / 10.34 / 11.86, plain
+//     depth 2 8.66 / 10.64 / 11.90; at 5 / 6 bits plain depth 1 with one wave
+//     more than the fewest 15.55 / 16.82 (early 16.19 / 17.81)
+//   4096 x 4096 (1 block per CU, 65 side-record entries per block): one wave
+//     more than the fewest, early depth 1 4.50 / 4.63 / 4.76 (the fewest waves,
+//     plain depth 2: 5.74 / 6.30 / 6.43)
+//   4096 x 14336 (1 block per CU, 229 entries per block): at 3 / 4 bits early
+//     depth 1 6.88 / 8.13 (plain depth 2 7.22 / 8.25); at 2 bits, the record
+//     applied after the loop, plain depth 2 6.72 (early 6.97, plain 1 7.18)
+//   5120 x 17920 (1.25 blocks per CU, 573 entries per block): plain depth 1 at
+//     every precision 10.92 / 12.44 / 13.83 / 19.17 / 20.33 (early 11.29 /
+//     12.91 / 15.95 / 20.30 / 21.01; plain depth 2 11.15 / 13.01 / 16.19)
+//   128256 x 4096 (31 blocks per CU) at 2 bits: early depth 1 36.9 us against
+//     about 34 with plain depth 2, which 14336 x 4096 ties (5.89 against 5.82)
+// So 2 bits keeps plain depth 2 (depth 1 on a heavy record after the loop), and
+// 3 and 4 bits issue early except for a heavy record on a small grid.  Early
+// issue is built for 3 and 4 bits, depth 2 for up to 3 bits.
+constexpr int kHeavySide = 256;   // side-record entries per block, on average, above which depth 1 is plain
 constexpr int kMaxWaves = 16;   // waves per workgroup (incl. a side-record wave): __launch_bounds__(1024)
 
 // LDS carve-up: per tile (padded tile columns, plus a spare tile) 64 dwords
@@ -1026,9 +1075,11 @@ static size_t lds_layout(int C, int S, bool cb, dev::GemvParams* prm) {
 // bits each wave takes the most steps it can (S = ceil(groups / 4): a wave
 // stages the x of at most 4 steps; measured on 14336 x 4096: 7.2 / 8.2 us at
 // 2 / 3 bits against 7.6 / 8.6 with two waves per SIMD; at 4 bits, with two
-// steps in flight, equal); from 5 bits S is the smallest count that puts
-// about two waves on every SIMD (8 per CU), within [ceil(groups / 4),
-// min(15, groups)].  The side record goes to the extra wave except for a
+// steps in flight, equal), except on grids of fewer than two blocks per CU
+// with a light record, which take one wave more (4096 x 4096, see the depth
+// notes above); from 5 bits S is the smallest count that puts about two waves
+// on every SIMD (8 per CU), one more on grids of two or more blocks per CU,
+// within [ceil(groups / 4), min(15, groups)].  The side record goes to the extra wave except for a
 // heavy CSR record (more than 128 entries per block on average) on a grid of
 // fewer than two workgroups per CU at 2 bits: there the main waves finish
 // soonest and the side wave's chain of dependent loads would set the launch's
@@ -1041,8 +1092,10 @@ static size_t lds_layout(int C, int S, bool cb, dev::GemvParams* prm) {
 // against 7.46 / 8.32 / 9.69.  With the record applied after the loop, each
 // wave takes at most 3 steps (4096 x 14336: 7.23 against 7.47 us with 4;
 // 5120 x 17920: 11.20 against 11.43, at 2 bits).
-// STAGQ_WAVES and STAGQ_SIDE override the choices (tuning); STAGQ_FLAG_SPINS
-// sets the side-record wave's spin limit (testing its global-x fallback).
+// STAGQ_WAVES, STAGQ_SIDE, STAGQ_DEPTH and STAGQ_EARLY override the choices
+// (tuning; a depth or issue mode that is not built for the precision is
+// ignored); STAGQ_FLAG_SPINS sets the side-record wave's spin limit (testing
+// its global-x fallback).
 constexpr int kLightSide = 128;   // side-record entries per block, on average, that the extra wave takes
 static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   const int T = h.cols / kTileCols;
@@ -1063,16 +1116,28 @@ static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   if (smin > smax) return false;
   const int target = 2 * 4 * cus;
   int S = (target + nblk - 1) / nblk;
-  if (side && bits <= 4) S = smin;
+  if (side && bits <= 4) S = smin + (!many && light && !h.side_slots ? 1 : 0);
+  if (side && bits >= 5 && many) S = std::max(S, smin + 1);
   if (!side) S = (Q + 2) / 3;          // after the loop: at most 3 steps per wave
   S = std::max(smin, std::min(smax, S));
   c->prm.flag_spins = env_int("STAGQ_FLAG_SPINS", dev::kFlagSpins);
   const int s_env = env_int("STAGQ_WAVES", 0);
   if (s_env) S = s_env;
   if (S < smin || S > smax) return false;
+  const bool heavy = !h.side_slots && h.nnz > int64_t(kHeavySide) * nblk;
+  int depth = 1;
+  bool early = false;
+  if (!side) depth = heavy || bits >= 4 ? 1 : 2;
+  else if (bits == 2) depth = 2;
+  else if (bits <= 4 && (many || !heavy)) early = true;
+  const int d_env = env_int("STAGQ_DEPTH", 0), e_env = env_int("STAGQ_EARLY", -1);
+  if (d_env == 1 || (d_env == 2 && bits <= 3)) depth = d_env;
+  if (e_env == 0 || (e_env == 1 && (bits == 3 || bits == 4))) early = e_env == 1;
+  if (early) depth = 1;
   c->S = S;
   c->side = side;
-  c->deep = many || light;
+  c->depth = depth;
+  c->early = early;
   c->grid = nblk;
   c->nt_max = (Q + S - 1) / S;
   c->lds = lds_layout(h.cols, S, h.codebook != 0, &c->prm);
@@ -1082,26 +1147,32 @@ static bool plan_gemv(const ImageHeader& h, int bits, LaunchCfg* c) {
   return true;
 }
 
-template <int M, int GU, int D>
+template <int M, int GU, int D, bool E>
 static hipError_t launch_gemv(const LaunchCfg& c, hipStream_t st) {
   const bool sc = c.prm.xsc != nullptr, cb = c.prm.table != nullptr;
   const dim3 grid(c.grid), block(64 * (c.S + (c.side ? 1 : 0)));
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, c.lds, st, c.prm); };
   if (c.side) {
-    if (cb) sc ? go(dev::gemv_kernel<M, GU, D, 1, true, true>) : go(dev::gemv_kernel<M, GU, D, 1, false, true>);
-    else sc ? go(dev::gemv_kernel<M, GU, D, 1, true, false>) : go(dev::gemv_kernel<M, GU, D, 1, false, false>);
+    if (cb) sc ? go(dev::gemv_kernel<M, GU, D, 1, true, true, E>) : go(dev::gemv_kernel<M, GU, D, 1, false, true, E>);
+    else sc ? go(dev::gemv_kernel<M, GU, D, 1, true, false, E>) : go(dev::gemv_kernel<M, GU, D, 1, false, false, E>);
   } else {
-    if (cb) sc ? go(dev::gemv_kernel<M, GU, D, 0, true, true>) : go(dev::gemv_kernel<M, GU, D, 0, false, true>);
-    else sc ? go(dev::gemv_kernel<M, GU, D, 0, true, false>) : go(dev::gemv_kernel<M, GU, D, 0, false, false>);
+    if (cb) sc ? go(dev::gemv_kernel<M, GU, D, 0, true, true, E>) : go(dev::gemv_kernel<M, GU, D, 0, false, true, E>);
+    else sc ? go(dev::gemv_kernel<M, GU, D, 0, true, false, E>) : go(dev::gemv_kernel<M, GU, D, 0, false, false, E>);
   }
   return hipGetLastError();
 }
 
+// Instantiated depths and issue modes: early issue up to 4 bits, depth 2 up
+// to 3 bits, plain depth 1 everywhere (plan_gemv picks only these).
 template <int M, int GU>
 static hipError_t launch_gemv_d(const LaunchCfg& c, hipStream_t st) {
-  // (the in-workgroup mode takes the shallower table: it runs for heavy
-  // records on smaller grids, or when forced)
-  return c.deep && c.side ? launch_gemv<M, GU, kDepthMany[M]>(c, st) : launch_gemv<M, GU, kDepthFew[M]>(c, st);
+  if constexpr (M == 3 || M == 4) {
+    if (c.early) return launch_gemv<M, GU, 1, true>(c, st);
+  }
+  if constexpr (M <= 3) {
+    if (c.depth == 2) return launch_gemv<M, GU, 2, false>(c, st);
+  }
+  return launch_gemv<M, GU, 1, false>(c, st);
 }
 
 template <int M>
@@ -1244,7 +1315,8 @@ int stagq_plan_gemv(int32_t rows, int32_t cols, int32_t group, int32_t nbits, in
   LaunchCfg c;
   if (!plan_gemv(H, bits, &c)) return STAGQ_ESHAPE;
   out[0] = c.grid; out[1] = 64 * (c.S + (c.side ? 1 : 0)); out[2] = c.S; out[3] = c.nt_max;
-  out[4] = kBlockRows; out[5] = int32_t(c.lds); out[6] = c.side ? 1 : 0; out[7] = c.deep && c.side ? kDepthMany[bits] : kDepthFew[bits];
+  out[4] = kBlockRows; out[5] = int32_t(c.lds); out[6] = c.side ? 1 : 0; out[7] = c.depth;
+  out[8] = c.early ? 1 : 0;
   return STAGQ_OK;
 }
 

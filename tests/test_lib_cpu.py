@@ -149,8 +149,8 @@ def test_validation_errors():
 
 def test_unsupported_shapes():
     for (R, Cc, g, N) in [(4, 100, 50, 4), (4, 256, 16, 4), (4, 256, 128, 9), (4, 256, 128, 1)]:
-        assert pwo.lib().stagq_plan_gemv(R, Cc, g, N, 0, 0, 2, (C.c_int32 * 8)()) == -3
-    assert pwo.lib().stagq_plan_gemv(4, 256, 128, 4, 0, 0, 5, (C.c_int32 * 8)()) == -2
+        assert pwo.lib().stagq_plan_gemv(R, Cc, g, N, 0, 0, 2, (C.c_int32 * 9)()) == -3
+    assert pwo.lib().stagq_plan_gemv(4, 256, 128, 4, 0, 0, 5, (C.c_int32 * 9)()) == -2
 
 
 def test_strerror_covers_every_status():
@@ -165,7 +165,7 @@ def test_launch_plan_shapes():
     than two blocks per CU at 2 bits; up to 4 bits each wave takes the most
     steps it can (4, as x is staged for at most 4 steps)."""
     def plan(R, Cc, bits, g=128, N=4, nnz=0, slots=0):
-        out = (C.c_int32 * 8)()
+        out = (C.c_int32 * 9)()
         assert pwo.lib().stagq_plan_gemv(R, Cc, g, N, nnz, slots, bits, out) == 0
         return dict(grid=out[0], threads=out[1], S=out[2], steps=out[3], side=out[6])
     p2, p4, p5 = plan(14336, 4096, 2), plan(14336, 4096, 4), plan(14336, 4096, 5, N=6)
@@ -173,7 +173,7 @@ def test_launch_plan_shapes():
     assert (p4["S"], p4["steps"], p4["threads"]) == (2, 4, 192)
     assert (p5["S"], p5["steps"], p5["threads"]) == (3, 3, 256)
     d = plan(4096, 14336, 2)
-    assert (d["grid"], d["S"], d["side"], d["threads"]) == (256, 7, 1, 512)   # no side record: light
+    assert (d["grid"], d["S"], d["side"], d["threads"]) == (256, 8, 1, 576)   # no side record: light, one wave more
     dh = plan(4096, 14336, 2, nnz=58720)           # 229 entries per block: after the loop,
     assert (dh["S"], dh["side"], dh["threads"]) == (10, 0, 640)   # at most 3 steps per wave
     assert plan(4096, 14336, 2, nnz=32768)["side"] == 1 and plan(4096, 14336, 2, nnz=32769)["side"] == 0
@@ -181,10 +181,17 @@ def test_launch_plan_shapes():
     assert plan(4096, 14336, 3, nnz=58720)["side"] == 1                  # heavy, small grid: 2 bits only
     d6 = plan(5120, 17920, 6, N=6, nnz=183501)     # 320 blocks, 35 groups of four tile columns
     assert (d6["grid"], d6["S"], d6["side"], d6["threads"]) == (320, 9, 1, 640)
-    out = (C.c_int32 * 8)()                        # steps in flight at 4 bits: 1 on smaller grids, 2 on many
-    assert pwo.lib().stagq_plan_gemv(5120, 17920, 128, 6, 183501, 0, 4, out) == 0 and (out[6], out[7]) == (1, 1)
-    assert pwo.lib().stagq_plan_gemv(14336, 4096, 128, 4, 58720, 0, 4, out) == 0 and (out[6], out[7]) == (1, 2)
-    assert pwo.lib().stagq_plan_gemv(4096, 4096, 128, 4, 16777, 0, 4, out) == 0 and (out[6], out[7]) == (1, 2)
+    out = (C.c_int32 * 9)()     # (side wave, depth, early issue) at 4 bits
+    assert pwo.lib().stagq_plan_gemv(5120, 17920, 128, 6, 183501, 0, 4, out) == 0 and tuple(out[6:9]) == (1, 1, 0)
+    assert pwo.lib().stagq_plan_gemv(14336, 4096, 128, 4, 58720, 0, 4, out) == 0 and tuple(out[6:9]) == (1, 1, 1)
+    assert pwo.lib().stagq_plan_gemv(4096, 4096, 128, 4, 16777, 0, 4, out) == 0 and tuple(out[6:9]) == (1, 1, 1)
+    assert out[2] == 3                              # few blocks per CU, light record: one wave more
+    assert pwo.lib().stagq_plan_gemv(14336, 4096, 128, 4, 58720, 0, 2, out) == 0 and tuple(out[6:9]) == (1, 2, 0)
+    assert pwo.lib().stagq_plan_gemv(14336, 4096, 128, 4, 58720, 0, 3, out) == 0 and tuple(out[6:9]) == (1, 1, 1)
+    assert pwo.lib().stagq_plan_gemv(4096, 14336, 128, 4, 58720, 0, 2, out) == 0 and tuple(out[6:9]) == (0, 2, 0)
+    assert pwo.lib().stagq_plan_gemv(5120, 17920, 128, 6, 183501, 0, 2, out) == 0 and tuple(out[6:9]) == (0, 1, 0)
+    assert pwo.lib().stagq_plan_gemv(17920, 5120, 128, 6, 183501, 0, 5, out) == 0 and tuple(out[6:9]) == (1, 1, 0)
+    assert out[2] == 4                              # many blocks per CU from 5 bits: one wave more than the fewest
     lm = plan(128256, 4096, 3)
     assert (lm["grid"], lm["S"], lm["side"]) == (8016, 2, 1)
 
@@ -389,7 +396,7 @@ def test_launch_plan_every_width_and_precision():
     steps of 128, every group size, N = 8 at every precision, with and without
     a heavy side record): the widest rows apply the side record after the loop
     when the extra wave does not fit."""
-    out = (C.c_int32 * 8)()
+    out = (C.c_int32 * 9)()
     for Cc in list(range(128, 32769, 128)):
         for g in (32, 64, 128):
             for bits in (2, 3, 4, 8):
