@@ -115,6 +115,21 @@ def cpu_baseline(rows_sample: int = 1024, target_s: float = 10.0):
     }
 
 
+INFINITY_CACHE_BYTES = 256 << 20   # MI355X last-level (Infinity) cache
+
+
+def rotation_copies(rot_mb: int, bytes_per_launch: int, minimum: int = 2) -> int:
+    """Image copies a timed run cycles through: enough that the bytes all copies
+    give the lowest precision read exceed rot_mb MB, which must be at least four
+    times the Infinity Cache, so no launch finds its bytes there (the FETCH_SIZE
+    counters count cache hits too; the rotation is what makes them HBM bytes)."""
+    if rot_mb * (1 << 20) < 4 * INFINITY_CACHE_BYTES:
+        raise ValueError(f"--rot-mb {rot_mb} is below 4 x the {INFINITY_CACHE_BYTES >> 20} MB Infinity Cache")
+    n = max(minimum, -(-rot_mb * (1 << 20) // bytes_per_launch))
+    assert n * bytes_per_launch >= 4 * INFINITY_CACHE_BYTES
+    return n
+
+
 def busy_gpu(ms: float = 2.0) -> None:
     """Queue a spin kernel of about ms milliseconds on the current stream, so the
     launches queued behind it (while it spins) start back to back instead of
@@ -149,6 +164,74 @@ def graph_time(launch, n_copies, K, bits_seq):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / (reps * n_copies)
+
+
+def eager_time(launch, n_copies, K, bits_seq):
+    """Mean microseconds per launch of K launches issued from Python (launch i
+    on copy i % n_copies, precision bits_seq[i % len]), one event pair around
+    them: a run that rocprofv3 counter collection can split per dispatch."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(K):
+        launch(i % n_copies, bits_seq[i % len(bits_seq)])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / K
+
+
+def cpu_baseline_sweep(args):
+    """The oracle (float64 decode by Eq. 9, side record, BLAS matvec) timed per
+    configuration shape and precision on the host: median of 3 calls with the
+    host's BLAS threads and one call on a single thread.  Fields come from the
+    oracle's own encoder (not timed).  One JSON line."""
+    import oracle
+    from workloads import WORKLOADS, synth_matrix
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threadpool_limits, blas = None, 1
+    cpu = ""
+    try:
+        cpu = next(ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name"))
+    except Exception:
+        pass
+    picks = [("tiny", "W"), ("attn", "qkvo"), ("layer_sweep", "k"), ("mlp", "gate_up"), ("mlp", "down"),
+             ("phi4_mlp", "gate_up"), ("phi4_mlp", "down"), ("layer_sweep", "lm_head")]
+    if args.workloads:
+        picks = [p for p in picks if p[0] in args.workloads.split(",")]
+    out = []
+    for wname, mname in picks:
+        wl = WORKLOADS[wname]
+        mat = [m for m in wl.matrices if m.name == mname][0]
+        w, x = synth_matrix(mat.rows, mat.cols, wl.dist, mat.seed)
+        t0 = time.perf_counter()
+        F = oracle.encode(w, wl.group, wl.nbits, wl.frac, wl.ratio_T)
+        t_enc = time.perf_counter() - t0
+        del w
+        for M in wl.bits:
+            runs = []
+            for _ in range(3):
+                r0 = time.perf_counter()
+                oracle.gemv(F, x, M)
+                runs.append(time.perf_counter() - r0)
+            one = None
+            if threadpool_limits is not None:
+                with threadpool_limits(limits=1, user_api="blas"):
+                    r0 = time.perf_counter()
+                    oracle.gemv(F, x, M)
+                    one = time.perf_counter() - r0
+            row = {"workload": wname, "matrix": mname, "rows": mat.rows, "cols": mat.cols, "bits": M,
+                   "us_all_threads": round(float(np.median(runs)) * 1e6, 1),
+                   "us_one_thread": round(one * 1e6, 1) if one else None, "encode_s": round(t_enc, 2)}
+            out.append(row)
+            print(f"[oracle] {wname}/{mname} {mat.rows}x{mat.cols} bits={M}: {row['us_all_threads']} us "
+                  f"({row['us_one_thread']} us on 1 thread)", file=sys.stderr, flush=True)
+        del F
+    print(json.dumps({"oracle_sweep": out, "blas_threads": int(blas), "cpu_count": os.cpu_count(),
+                      "affinity": len(os.sched_getaffinity(0)), "cpu_model": cpu}), flush=True)
 
 
 def codebook_fields(fields):
@@ -253,7 +336,11 @@ def sweep(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     rows = []
-    for wname in ("attn", "mlp", "mlp_rows", "phi4_mlp", "layer_sweep"):
+    timer = graph_time if args.mode == "graph" else eager_time
+    names = ("attn", "mlp", "mlp_rows", "phi4_mlp", "layer_sweep")
+    if args.workloads:
+        names = tuple(n for n in names if n in args.workloads.split(","))
+    for wname in names:
         wl = WORKLOADS[wname]
         for mat in wl.matrices:
             w, x = synth_matrix(mat.rows, mat.cols, wl.dist, mat.seed)
@@ -261,10 +348,10 @@ def sweep(args):
             fields = pwo.encode(w, wl.group, wl.nbits, K, wl.ratio_T, post_per_row=wl.post_per_row)
             del w
             base = pwo.StagQMatrix.pack(fields, device=dev)
-            slm = pwo.StagQMatrix.pack(fields, device=dev, side_slots=-1) if wl.post_per_row else None
-            cbm = pwo.StagQMatrix.pack(codebook_fields(fields), device=dev) if wname == "mlp" else None
+            slm = pwo.StagQMatrix.pack(fields, device=dev, side_slots=-1) if wl.post_per_row and not args.plain else None
+            cbm = pwo.StagQMatrix.pack(codebook_fields(fields), device=dev) if wname == "mlp" and not args.plain else None
             del fields
-            n_copies = max(2, -(-args.rot_mb * (1 << 20) // base.bytes_read[min(wl.bits)]))
+            n_copies = rotation_copies(args.rot_mb, base.bytes_read[min(wl.bits)])
             copies = [base] + [base.replicate() for _ in range(n_copies - 1)]
             xd = torch.from_numpy(x.view(np.int16)).view(torch.float16).to(dev)
             ys = [torch.empty(mat.rows, dtype=torch.float32, device=dev) for _ in range(n_copies)]
@@ -278,12 +365,12 @@ def sweep(args):
             entry = {"workload": wname, "matrix": mat.name, "rows": mat.rows, "cols": mat.cols,
                      "nnz": int(base.nnz), "copies": n_copies, "bits": {}}
             for M in wl.bits:
-                us = graph_time(launch, n_copies, args.steps, [M])
+                us = timer(launch, n_copies, args.steps, [M])
                 b = base.bytes_read[M]
                 entry["bits"][str(M)] = {"us": round(us, 3), "bytes": int(b), "gbps": round(b / us / 1e3, 1),
                                          "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2),
                                          "launch": base.plan(M)}
-            if wname == "mlp":
+            if wname == "mlp" and not args.plain:
                 # the same GEMVs with the inverse AWQ scale applied to x (stagq_gemv_scaled)
                 sc = torch.from_numpy(np.full(mat.cols, 0.5, np.float16).view(np.int16)).view(torch.float16).to(dev)
 
@@ -291,7 +378,7 @@ def sweep(args):
                     copies[c].gemv(xd, M, y=ys[c], x_scale=sc)
 
                 for M in wl.bits:
-                    us = graph_time(launch_sc, n_copies, args.steps, [M])
+                    us = timer(launch_sc, n_copies, args.steps, [M])
                     entry["bits"][str(M)]["awq_scaled_us"] = round(us, 3)
                 # the same GEMVs with an fp16 result (stagq_gemv_f16)
                 y16 = [torch.empty(mat.rows, dtype=torch.float16, device=dev) for _ in range(n_copies)]
@@ -300,7 +387,7 @@ def sweep(args):
                     copies[c].gemv(xd, M, y=y16[c])
 
                 for M in wl.bits:
-                    us = graph_time(launch_h, n_copies, args.steps, [M])
+                    us = timer(launch_h, n_copies, args.steps, [M])
                     entry["bits"][str(M)]["fp16_out_us"] = round(us, 3)
                 del y16
                 # the same GEMVs on codebook metadata (1 byte per group + 256 pairs)
@@ -310,7 +397,7 @@ def sweep(args):
                     cbc[c].gemv(xd, M, y=ys[c])
 
                 for M in wl.bits:
-                    us = graph_time(launch_cb, n_copies, args.steps, [M])
+                    us = timer(launch_cb, n_copies, args.steps, [M])
                     b = cbm.bytes_read[M]
                     entry["bits"][str(M)]["codebook"] = {"us": round(us, 3), "bytes": int(b),
                                                          "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2)}
@@ -323,14 +410,14 @@ def sweep(args):
                     slc[c].gemv(xd, M, y=ys[c])
 
                 for M in wl.bits:
-                    us = graph_time(launch_sl, n_copies, args.steps, [M])
+                    us = timer(launch_sl, n_copies, args.steps, [M])
                     b = slm.bytes_read[M]
                     entry["bits"][str(M)]["slots"] = {"us": round(us, 3), "bytes": int(b), "W": slm.side_slots,
                                                       "pct_peak": round(100 * b / us / 1e3 / PEAK_HBM_GBS, 2)}
                 del slc
             del slm
-            if wname == "layer_sweep":
-                us = graph_time(launch, n_copies, args.steps, list(wl.bits))
+            if wname == "layer_sweep" and not args.plain:
+                us = timer(launch, n_copies, args.steps, list(wl.bits))
                 b = sum(base.bytes_read[M] for M in wl.bits) / len(wl.bits)
                 entry["switched_2_3_4"] = {"us_per_call": round(us, 3), "gbps": round(b / us / 1e3, 1)}
             rows.append(entry)
@@ -345,7 +432,7 @@ def sweep(args):
             del copies, base, ys
             torch.cuda.empty_cache()
     print(json.dumps({"metric": METRIC, "sweep": rows, "steps": args.steps, "warmup": args.warmup,
-                      "mode": "graph", "data": "synthetic"}), flush=True)
+                      "mode": args.mode, "data": "synthetic"}), flush=True)
 
 
 HEADLINE = ("mlp", "gate_up")      # the Llama-3.1-8B gate/up projection, 14336 x 4096
@@ -423,6 +510,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="time every matrix of every workload instead of the headline line")
+    ap.add_argument("--workloads", default="",
+                    help="--sweep / --oracle-sweep: comma-separated workload names to run (default all)")
+    ap.add_argument("--plain", action="store_true",
+                    help="--sweep: only the plain GEMV per matrix (no AWQ, fp16-output, codebook, slot "
+                         "or switched-precision variants)")
+    ap.add_argument("--oracle-sweep", action="store_true",
+                    help="time the CPU oracle per configuration shape and precision (host only)")
     ap.add_argument("--read-sweep", action="store_true",
                     help="time plain reads of the headline byte counts and of the LM head's over a "
                          "grid of launch shapes (threads, loads in flight, workgroups)")
@@ -433,6 +527,10 @@ def main():
         print("bench.py: the GEMV runs on one GPU only; --gpus must be 1 (the GEMV path has "
               "no multi-GPU leg).", file=sys.stderr)
         sys.exit(2)
+
+    if args.oracle_sweep:
+        cpu_baseline_sweep(args)
+        return
 
     import torch
     import precision_weight_only_amd as pwo
@@ -459,7 +557,7 @@ def main():
     base = pwo.StagQMatrix.pack(fields, device=dev)
     # Enough copies that the lowest precision's reads of all of them exceed
     # the rotation size, and every precision cycles through all of them.
-    n_copies = max(6, -(-args.rot_mb * (1 << 20) // base.bytes_read[min(bits)]))
+    n_copies = rotation_copies(args.rot_mb, base.bytes_read[min(bits)], minimum=6)
     copies = [base] + [base.replicate() for _ in range(n_copies - 1)]
     xd = torch.from_numpy(x.view(np.int16)).view(torch.float16).to(dev)
     ys = [torch.empty(R, dtype=torch.float32, device=dev) for _ in range(n_copies)]

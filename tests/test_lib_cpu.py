@@ -459,3 +459,17 @@ def test_bench_codebook_fields_select_the_oracle_pairs():
     back = pwo.unpack_host(img)
     assert back["codebook"] == 1
     assert np.array_equal(back["lo"].view(np.uint16), np.asarray(cb["lo"], np.float16).view(np.uint16))
+
+
+def test_bench_rotation_exceeds_the_infinity_cache():
+    """Timed runs cycle through enough image copies that no launch can find its
+    bytes in the 256 MB Infinity Cache: the headline's 63 copies at 2 bits hold
+    over 1 GB, every shape's rotation holds at least 4 x the cache, and a
+    rotation below that is refused."""
+    import bench
+    assert bench.rotation_copies(1024, 17107716, minimum=6) == 63
+    for b in (1229588, 4893772, 17107716, 27426412, 152987852):
+        n = bench.rotation_copies(1024, b)
+        assert n * b >= 1024 << 20 and n >= 2
+    with pytest.raises(ValueError):
+        bench.rotation_copies(512, 17107716)
