@@ -473,6 +473,7 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
     uint64_t ent[kSideBatches];
 #pragma unroll
     for (int j = 0; j < kSideBatches; j++) {
+      if (cb + 64 * j >= E1) break;      // only the batches that hold entries (uniform)
       const int e = cb + 64 * j + lane;
       ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
     }
@@ -482,12 +483,14 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
     if (use_lds) {
 #pragma unroll
       for (int j = 0; j < kSideBatches; j++) {
+        if (cb + 64 * j >= E1) break;    // (uniform)
         const int c = cb + 64 * j + lane < E1 ? int(ent[j] >> 48) : 0;
         xc[j] = xh[(c >> 7) * (2 * kXPitch) + (c & 127)];
       }
     } else {
 #pragma unroll
       for (int j = 0; j < kSideBatches; j++) {
+        if (cb + 64 * j >= E1) break;    // (uniform)
         const int e = cb + 64 * j + lane;
         xc[j] = ld16(rX, e < E1 ? uint32_t(ent[j] >> 48) * 2u : kOOB);
       }
@@ -495,6 +498,7 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
         const rsrc_t rS = mk(p.xsc, p.x_bytes);
 #pragma unroll
         for (int j = 0; j < kSideBatches; j++) {
+          if (cb + 64 * j >= E1) break;  // (uniform)
           const int e = cb + 64 * j + lane;
           xc[j] = hmul2(xc[j], ld16(rS, e < E1 ? uint32_t(ent[j] >> 48) * 2u : kOOB)) & 0xffffu;
         }
@@ -710,15 +714,17 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
   //     is sunk into a branch.  Only this wave reads these before the barrier.
   constexpr int kCpg = 16 / GU;
   const int li = lane & (kCpg - 1);
+  // chunk cbase + lane + 64 k is chunk lane & 15 of tile 4 (q0 + k) + lane / 16:
+  // the lane's part of both LDS addresses is fixed, the tile's is wave-uniform
+  const int xl = (lane >> 4) * kXPitch + (lane & 15) * 4;
+  const int sxl = li == kCpg - 1 ? (lane >> 4) * kXPitch + 64 + (lane & 15) / kCpg : -1;
+  const int spare = p.T4 * kXPitch;
 #pragma unroll
   for (int k = 0; k < kXChunks; k++) {
     if (64 * k >= nch) break;            // the wave's x ends here (uniform)
-    const int c = lane + 64 * k;
-    const bool ok = c < nch;
-    const int ci = cbase + c;
-    // (a 24-bit multiply: a 32-bit one becomes a 64-bit multiply-add whose
-    // unused high addend can land on a pending load's register and wait for it)
-    const int xo = ok ? int(__umul24(uint32_t(ci >> 4), uint32_t(kXPitch))) + (ci & 15) * 4 : p.T4 * kXPitch;
+    const bool ok = lane + 64 * k < nch;
+    const int tb = __builtin_amdgcn_readfirstlane((4 * q0 + 4 * k) * kXPitch);
+    const int xo = ok ? tb + xl : spare;
     if constexpr (SC) {
 #pragma unroll
       for (int i = 0; i < 4; i++) xv[k][i] = hmul2(xv[k][i], av[k][i]);
@@ -734,9 +740,9 @@ __global__ void __launch_bounds__(1024) gemv_kernel(const GemvParams p) {
     u = row_shr_add<2>(v); v = kCpg == 16 || li >= 2 ? u : v;
     if constexpr (kCpg >= 8) { u = row_shr_add<4>(v); v = kCpg == 16 || li >= 4 ? u : v; }
     if constexpr (kCpg >= 16) { u = row_shr_add<8>(v); v = u; }
-    // sum(x) of group (ci & 15) / kCpg of tile ci / 16 sits after the tile's x
-    // (spare lanes write into the spare tile)
-    xs[(ok && li == kCpg - 1 ? (ci >> 4) : p.T4) * kXPitch + 64 + (ci & 15) / kCpg] = __builtin_bit_cast(uint32_t, v);
+    // sum(x) of the lane's group sits after its tile's x (the other lanes, and
+    // lanes past the wave's x, write into the spare tile)
+    xs[ok && sxl >= 0 ? tb + sxl : spare + 64] = __builtin_bit_cast(uint32_t, v);
   }
   if constexpr (!SIDE) rp_s[w == 0 && lane <= 16 ? lane : 17] = int32_t(rpv);
   if constexpr (CB) *reinterpret_cast<u32x4*>(tab_s + 4 * lane) = tabv;
