@@ -242,20 +242,27 @@ __device__ __forceinline__ void quarter(const Slot<M, GU>& s, int d, const uint3
     }
   };
   if constexpr (M == 2) {
-    // fields j = 0..4 in place (value q 2^(2j) 2^-24), 5..7 after a shift by 6
+    // fields j = 0..4 in place (value q 2^(2j) 2^-24), 5..7 after a shift by 6.
+    // A dword's eight masks issue before its eight products: alternating the
+    // two costs about 10% more issue cycles per wave step (measured with two
+    // waves per SIMD), 0.06 us per launch on 14336 x 4096.
 #pragma unroll
     for (int e = 0; e < 2; e++) {
       const uint32_t w = s0_dword(s.a, s.b, 2 * d + e);
       const uint32_t* x8 = xq + 8 * e;
-      mac(0, w & 0x00030003u, x8[0]);
-      mac(1, w & 0x000C000Cu, x8[1]);
-      mac(2, w & 0x00300030u, x8[2]);
-      mac(3, w & 0x00C000C0u, x8[3]);
-      mac(4, w & 0x03000300u, x8[4]);
       const uint32_t t = w >> 6;
-      mac(2, t & 0x00300030u, x8[5]);
-      mac(3, t & 0x00C000C0u, x8[6]);
-      mac(4, t & 0x03000300u, x8[7]);
+      const uint32_t m[8] = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u, w & 0x00C000C0u,
+                             w & 0x03000300u, t & 0x00300030u, t & 0x00C000C0u, t & 0x03000300u};
+      __builtin_amdgcn_sched_barrier(0);
+      mac(0, m[0], x8[0]);
+      mac(1, m[1], x8[1]);
+      mac(2, m[2], x8[2]);
+      mac(3, m[3], x8[3]);
+      mac(4, m[4], x8[4]);
+      mac(2, m[5], x8[5]);
+      mac(3, m[6], x8[6]);
+      mac(4, m[7], x8[7]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     uint32_t ye, yo;
