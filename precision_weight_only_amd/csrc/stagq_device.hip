@@ -480,7 +480,6 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
     uint64_t ent[kSideBatches];
 #pragma unroll
     for (int j = 0; j < kSideBatches; j++) {
-      if (cb + 64 * j >= E1) break;      // only the batches that hold entries (uniform)
       const int e = cb + 64 * j + lane;
       ent[j] = ld64side(rSide, e < E1 ? uint32_t(e) * 8u : kOOB);
     }
@@ -490,14 +489,12 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
     if (use_lds) {
 #pragma unroll
       for (int j = 0; j < kSideBatches; j++) {
-        if (cb + 64 * j >= E1) break;    // (uniform)
         const int c = cb + 64 * j + lane < E1 ? int(ent[j] >> 48) : 0;
         xc[j] = xh[(c >> 7) * (2 * kXPitch) + (c & 127)];
       }
     } else {
 #pragma unroll
       for (int j = 0; j < kSideBatches; j++) {
-        if (cb + 64 * j >= E1) break;    // (uniform)
         const int e = cb + 64 * j + lane;
         xc[j] = ld16(rX, e < E1 ? uint32_t(ent[j] >> 48) * 2u : kOOB);
       }
@@ -505,7 +502,6 @@ __device__ __forceinline__ void side_record(const GemvParams& p, int blk, int la
         const rsrc_t rS = mk(p.xsc, p.x_bytes);
 #pragma unroll
         for (int j = 0; j < kSideBatches; j++) {
-          if (cb + 64 * j >= E1) break;  // (uniform)
           const int e = cb + 64 * j + lane;
           xc[j] = hmul2(xc[j], ld16(rS, e < E1 ? uint32_t(ent[j] >> 48) * 2u : kOOB)) & 0xffffu;
         }
