@@ -50,8 +50,8 @@ class Info(C.Structure):
 def _load() -> C.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m precision_weight_only_amd.build` "
-            "(or __graft_entry__.build()).  There is no fallback path.")
+            f"{LIB_PATH} is missing: build it with `python -m precision_weight_only_amd.build`.  "
+            "There is no fallback path.")
     lib = C.CDLL(LIB_PATH)
     P = C.c_void_p
     sig = {
