@@ -360,6 +360,9 @@ EDGE = [
     (300, 1024, 128, 8, 0.005, "student_t", 4),    # N = 8: every precision 2..8
     (64, 4096, 128, 4, 0.1, "student_t", 5),       # more entries than one prefetched chunk
     (513, 8320, 64, 5, 0.001, "student_t", 6),     # 65 tiles per row (> one wave)
+    (40, 32768, 128, 4, 0.001, "student_t", 7),    # the widest rows: 16 main waves, record after the loop
+    (17, 30720, 64, 4, 0.002, "student_t", 8),     # the widest rows that keep the side-record wave (3-4 bits)
+    (3, 32768, 32, 6, 0.01, "normal_outliers", 9),  # g = 32, N = 6 at the widest rows, one block
 ]
 
 
