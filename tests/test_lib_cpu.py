@@ -473,3 +473,18 @@ def test_bench_rotation_exceeds_the_infinity_cache():
         assert n * b >= 1024 << 20 and n >= 2
     with pytest.raises(ValueError):
         bench.rotation_copies(512, 17107716)
+
+
+def test_bench_traffic_profile_matches_the_kernel(monkeypatch):
+    """The committed FETCH_SIZE / WRITE_SIZE summary was taken on the current
+    kernel source (so the bench line reports it), holds a value per headline
+    precision within a few percent above the algorithmic bytes, and is ignored
+    once the source changes."""
+    import bench
+    t = bench.read_traffic()
+    assert t is not None, "profiles/gemv_14336x4096_traffic.md is stale for stagq_device.hip"
+    alg = {2: 17107716, 3: 24447748, 4: 31787780}
+    for M, b in alg.items():
+        assert 1.0 <= t[M] / b <= 1.05
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.read_traffic() is None
