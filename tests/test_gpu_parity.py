@@ -293,6 +293,35 @@ def test_gemv_decode_one_hot(pwo, workload, mname):
         _say(f"one-hot {workload}/{mname}", f"bits={M}: {n_codes} codes exact, {n_held} held-out entries")
 
 
+ONEHOT_SMALL = [
+    # (rows, cols, group, nbits, frac, dist, seed, codebook)
+    (300, 1024, 128, 8, 0.005, "student_t", 4, False),      # every precision 2..8 (planes 3..8)
+    (77, 640, 32, 6, 0.02, "normal_outliers", 3, False),   # g = 32: four groups per tile
+    (1001, 384, 64, 4, 0.01, "student_t", 2, False),       # g = 64: two groups per tile, ragged rows
+    (300, 1024, 64, 7, 0.005, "student_t", 11, True),      # codebook metadata, odd N
+]
+
+
+@pytest.mark.parametrize("case", ONEHOT_SMALL,
+                         ids=[f"{c[0]}x{c[1]}g{c[2]}N{c[3]}{'cb' if c[7] else ''}" for c in ONEHOT_SMALL])
+def test_gemv_decode_one_hot_groups_and_precisions(pwo, case):
+    """The GEMV's own decode code by code (one-hot x over every column) where
+    the full-size matrices do not reach: groups of 32 and 64 columns (several
+    (lo, s) pairs per tile), every precision up to 8 bits (the plane-pair and
+    odd-plane merges of Eq. 8), and codebook metadata (the pair looked up by
+    the group's index)."""
+    R, Cc, g, N, frac, dist, seed, cb = case
+    w, _ = synth_matrix(R, Cc, dist, seed)
+    F = oracle.encode(w, g, N, frac)
+    if cb:
+        F = _codebook_reindex(F)
+    m = pwo.StagQMatrix.pack(F)
+    tiles = list(range(Cc // 128))
+    for M in range(2, N + 1):
+        _say(f"one-hot {case}", f"bits={M}")
+        _onehot_check(m, F, M, tiles, f"one-hot {case}")
+
+
 def _codebook_reindex(F):
     """Fields of the same main stream and side record with codebook metadata:
     two 16-entry fp16 codebooks placed uniformly over the fields' log2 s and
